@@ -1,0 +1,185 @@
+"""Quantizers: float values -> (codes, scales).  TEST INFRASTRUCTURE ONLY.
+
+All arithmetic is numpy float32 (IEEE-754, round to nearest even, true
+division), which is the precision the pages state for these steps.
+
+fp8_rowblock / fp8_tile
+    atrex-bench block_scaled_mm, "Input Generation": per block, absmax,
+    scale = max(absmax / 448, 1e-10) in float32, codes = e4m3fn(clamp(x /
+    scale, -448, 448)).  Activations use 1 x group_k blocks along each row,
+    weights group_n x group_k tiles.  Reading: the page takes the weight
+    tile's max without abs(); the activation path and the workload
+    description both use the absolute maximum, which is the reading taken
+    here for both (a signed max would let negative outliers clip).
+    Parity pinned by invariants (the pages print no quantized values).
+
+int8_rows / int8_cols
+    TensorTonic "Int8 Matmul with Per-Channel Scales": s = max|v| / 127 per
+    row of x and per column of w, s = 1 for an all-zero row or column,
+    q = clip(round(v / s), -127, 127) with round = nearest, ties to even
+    (the problem's hint names jnp.round, which rounds half to even).
+    Pinned by the three printed examples.
+
+mx
+    MX blocks of 32 along the contraction axis with an e8m0 scale
+    (jax.nn.scaled_matmul Notes, mxfp8; NKI backward, float8_dtype).  The
+    pages do not state how the scale is chosen.  Reading: keep the
+    block_scaled_mm rule (scale >= absmax / fmax, absmax floored at 1e-10)
+    and restrict the scale to a power of two by rounding it up: E is the
+    smallest integer with absmax <= fmax * 2^E, clamped to [-127, 127],
+    scale byte = E + 127, codes = fp8(clamp(x * 2^-E, +-fmax)).  No element
+    ever clips.  ``rule="ocp"`` gives the OCP-style alternative
+    E = floor(log2 absmax) - emax_elem with saturation, for comparison only.
+    Parity unpinned by the pages for the scale rule itself; pinned by
+    invariants and by the power-of-two special case that coincides with
+    fp8_rowblock.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats as F
+
+F32_1E_10 = np.float32(1e-10)
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+# ------------------------------------------------------- fp8, fp32 scales ---
+
+def fp8_rowblock(x: np.ndarray, group: int = 128, fmt: str = F.E4M3):
+    """1 x ``group`` blocks along each row of x[R, C].
+
+    Returns (codes uint8 [R, C], scales float32 [R, C // group]).
+    """
+    x = _f32(x)
+    R, C = x.shape
+    if C % group:
+        raise ValueError("cols must be a multiple of group")
+    top = np.float32(F.fmax(fmt))
+    xb = x.reshape(R, C // group, group)
+    amax = np.max(np.abs(xb), axis=2) if R and C else np.zeros((R, C // group), np.float32)
+    s = np.maximum(amax / top, F32_1E_10).astype(np.float32)
+    v = (xb / s[:, :, None]).astype(np.float32)
+    v = np.clip(v, -top, top)
+    codes = F.encode(v, fmt).reshape(R, C)
+    return codes, s
+
+
+def fp8_tile(x: np.ndarray, group_r: int = 128, group_c: int = 128, fmt: str = F.E4M3):
+    """``group_r`` x ``group_c`` tiles of x[R, C], one scale per tile.
+
+    Returns (codes uint8 [R, C], scales float32 [R // group_r, C // group_c]).
+    """
+    x = _f32(x)
+    R, C = x.shape
+    if R % group_r or C % group_c:
+        raise ValueError("shape must be a multiple of the tile")
+    top = np.float32(F.fmax(fmt))
+    xt = x.reshape(R // group_r, group_r, C // group_c, group_c)
+    amax = np.max(np.abs(xt), axis=(1, 3))
+    s = np.maximum(amax / top, F32_1E_10).astype(np.float32)
+    v = (xt / s[:, None, :, None]).astype(np.float32)
+    v = np.clip(v, -top, top)
+    codes = F.encode(v, fmt).reshape(R, C)
+    return codes, s
+
+
+# --------------------------------------------------------- int8 per-channel -
+
+def _int8_along(v: np.ndarray, axis: int):
+    amax = np.max(np.abs(v), axis=axis, keepdims=True)
+    s = np.where(amax == 0, np.float32(1.0), amax / np.float32(127.0)).astype(np.float32)
+    r = np.rint((v / s).astype(np.float32))
+    q = np.clip(r, -127, 127).astype(np.int8)
+    return q, np.squeeze(s, axis=axis)
+
+
+def int8_rows(x: np.ndarray):
+    """x[B, D_in] -> (x_q int8 [B, D_in], x_scales float32 [B]); one scale
+    per row."""
+    return _int8_along(_f32(x), axis=1)
+
+
+def int8_cols(w: np.ndarray):
+    """w[D_in, D_out] -> (w_q int8 [D_in, D_out], w_scales float32 [D_out]);
+    one scale per column, codes keep w's layout."""
+    return _int8_along(_f32(w), axis=0)
+
+
+# ---------------------------------------------------------------- MX ------
+
+def _exponent_fields(a: np.ndarray):
+    """For positive normal float32 a: (e, mant_bits) with a = (1 + f) 2^e,
+    read from the IEEE fields (no log2)."""
+    u = _f32(a).view(np.uint32)
+    e = ((u >> 23) & 0xFF).astype(np.int64) - 127
+    mant = (u & 0x7FFFFF).astype(np.int64)
+    return e, mant
+
+
+def mx_scale_exponent(amax: np.ndarray, fmt: str, rule: str = "ceil") -> np.ndarray:
+    """Block scale exponent E (int64) for float32 block maxima."""
+    amax = np.maximum(_f32(amax), F32_1E_10)
+    e, mant = _exponent_fields(amax)
+    if rule == "ceil":
+        # smallest E with amax <= fmax * 2^E, computed exactly: fmax is
+        # 1.75 * 2^emax_elem for both formats, so with amax = (1+f) 2^e the
+        # answer is e - emax_elem, plus one when 1+f exceeds 1.75.
+        top = F.fmax(fmt)
+        emax_elem = int(np.floor(np.log2(top)))
+        top_mant = top / 2.0 ** emax_elem  # 1.75
+        top_mant_bits = int(round((top_mant - 1.0) * (1 << 23)))
+        E = e - emax_elem + (mant > top_mant_bits).astype(np.int64)
+        # exact cross-check of the defining inequality (float64 holds all)
+        a64 = amax.astype(np.float64)
+        assert np.all(a64 <= top * np.exp2(E.astype(np.float64)))
+        assert np.all(a64 > top * np.exp2(E.astype(np.float64) - 1))
+    elif rule == "ocp":
+        emax_elem = {F.E4M3: 8, F.E5M2: 15}[fmt]
+        E = e - emax_elem
+    else:
+        raise ValueError(rule)
+    return np.clip(E, -127, 127)
+
+
+def mx(x: np.ndarray, fmt: str = F.E4M3, block: int = 32, rule: str = "ceil"):
+    """MX quantization of x[..., C] with ``block``-element blocks along the
+    last axis.
+
+    Returns (codes uint8 [..., C], scale bytes uint8 [..., C // block]).
+    Callers that block along another axis transpose first (``mx_axis``).
+    """
+    x = _f32(x)
+    C = x.shape[-1]
+    if C % block:
+        raise ValueError("blocked dim must be a multiple of the block")
+    lead = x.shape[:-1]
+    xb = x.reshape(*lead, C // block, block)
+    amax = np.max(np.abs(xb), axis=-1) if xb.size else np.zeros((*lead, C // block), np.float32)
+    E = mx_scale_exponent(amax, fmt, rule)
+    # x * 2^-E is exact in float32 for every value that stays normal; those
+    # that underflow encode to a signed zero either way.
+    v = np.ldexp(xb, (-E)[..., None].astype(np.int32)).astype(np.float32)
+    top = np.float32(F.fmax(fmt))
+    v = np.clip(v, -top, top)
+    codes = F.encode(v, fmt).reshape(x.shape)
+    scales = (E + 127).astype(np.uint8)
+    return codes, scales
+
+
+def mx_axis(x2d: np.ndarray, axis: int, fmt: str = F.E4M3, block: int = 32):
+    """MX-quantize a matrix with blocks running along ``axis``.
+
+    axis = 1: blocks along each row; codes [R, C], scales [R, C/32].
+    axis = 0: blocks along each column; the result is laid out transposed,
+              codes [C, R], scales [C, R/32] (blocks contiguous).
+    """
+    x2d = _f32(x2d)
+    if axis == 1:
+        return mx(x2d, fmt, block)
+    if axis == 0:
+        return mx(np.ascontiguousarray(x2d.T), fmt, block)
+    raise ValueError(axis)
