@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 hot path on one MI355X.
+
+Default (the one JSON line on stdout):
+    python bench.py [--steps K] [--warmup W]
+A step is one pass of the FP8 block_scaled_mm path at m = n = k = 4096,
+group_n = group_k = 128: quantize the float32 activations (1 x 128 blocks,
+E4M3 + float32 scales), quantize the float32 weights (128 x 128 tiles), then
+the block-scaled GEMM with its fused float32 epilogue.  Inputs are resident
+in HBM before timing; four input sets are rotated so that the 256 MB
+last-level cache cannot serve the quantizers' reads.  `value` is the GEMM's
+algorithmic 2 m n k FLOPs per step time (TFLOP/s).  The JSON line also
+carries the GEMM kernel's own roofline (HIP events around each of its
+launches, on the launch stream) and the CPU oracle timed on a bounded
+sample on this host.
+
+    python bench.py --suite [--out FILE]
+times every kernel of the path at its own workload (quantizers, FP8 GEMM
+sweep, INT8 per-channel, MXFP8 batched, MXFP8 backward) and writes one JSON
+object per kernel to FILE (default gpurun_out/suite.jsonl).
+
+One GPU only: --gpus N with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s & % of FP8 MFMA peak, block-scaled GEMM m=n=k=4096 group 128"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# block_scaled_mm row 14 (m = n = k = 4096): T_Prod = 1.06 ms on unstated
+# hardware, i.e. 2 * 4096^3 / 1.06 ms = 129.66 TFLOP/s (GEMM only).
+PAGE_T_PROD_TFLOPS_4096 = 2 * 4096 ** 3 / 1.06e-3 / 1e12
+GEMM_SRC = os.path.join(ROOT, "block_scaled_precision_blockwise_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_4096_traffic.json")
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _gpu_setup():
+    import torch
+    import block_scaled_precision_blockwise_amd as bsq
+
+    if not bsq.is_built():
+        import __graft_entry__
+        __graft_entry__.build()
+    torch.cuda.set_device(0)
+    bsq.bsq_device_check()
+    return torch, bsq
+
+
+class KernelTimer:
+    """HIP events around individual launches on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def around(self, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(len(self.pairs), 1)
+
+
+# --------------------------------------------------------------- main ----
+
+def run_main(args):
+    torch, bsq = _gpu_setup()
+    import numpy as np
+    import synth
+
+    M = N = K = 4096
+    dev = torch.device("cuda:0")
+    _log(f"[bench] main step: quant 1x128 + quant 128x128 + GEMM at {M}x{N}x{K}")
+    sets = []
+    for i in range(4):
+        a32, b32 = synth.fp8_blockwise_raw(M, N, K, 204 + 2 * i, 205 + 2 * i)
+        sets.append((torch.from_numpy(a32).to(dev), torch.from_numpy(b32).to(dev)))
+    aq = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    bq = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    sb = torch.empty(N // 128, K // 128, dtype=torch.float32, device=dev)
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    gemm_t = KernelTimer(torch)
+
+    def step(i, timed):
+        a, b = sets[i % len(sets)]
+        bsq.bsq_quant_fp8_rowblock(a, aq, sa, 128)
+        bsq.bsq_quant_fp8_tile(b, bq, sb, 128, 128)
+        if timed:
+            gemm_t.around(lambda: bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y))
+        else:
+            bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i, True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = 2.0 * M * N * K
+    value = flops / (ms * 1e-3) / 1e12
+    gemm_ms = gemm_t.mean_ms()
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    _log(f"[bench] step {ms * 1e3:.1f} us -> {value:.1f} TFLOP/s; GEMM alone {gemm_ms * 1e3:.1f} us "
+         f"-> {gemm_tflops:.1f} TFLOP/s ({100 * gemm_tflops / PEAK_FP8_TFLOPS:.1f}% of FP8 peak)")
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("gemm_src_sha256_16") == _src_hash(GEMM_SRC):
+            traffic = tr.get("bytes_per_launch")
+    except (OSError, ValueError):
+        traffic = None
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGE_T_PROD_TFLOPS_4096, 3),
+        "vs_baseline_ref": "block_scaled_mm row 14 T_Prod 1.06 ms (GEMM only, unstated hardware) = "
+                           f"{PAGE_T_PROD_TFLOPS_4096:.1f} TFLOP/s; our value includes both quantizers",
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "pct_of_fp8_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "config": {
+            "workload": "block_scaled_mm FP8 e4m3, m=n=k=4096, group_n=group_k=128, fp32 out; "
+                        "step = 1x128 activation quant + 128x128 weight quant + GEMM",
+            "m": M, "n": N, "k": K, "group_n": 128, "group_k": 128,
+            "inputs": "randn float32 (PCG64 seeds 204..211), 4 rotating sets",
+        },
+        "roofline": {
+            "kernel": "k_gemm<FP8G> (block-scaled GEMM, fused fp32 epilogue)",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gemm_ms * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline():
+    """The oracle as written, on one whole step of the same workload: both
+    quantizers, then the oracle GEMM (its float64 product and its
+    error-bound product).  About 10 s on 8 cores; reported as TFLOP/s on
+    the GEMM's 2 m n k."""
+    import numpy as np
+    import synth
+    from oracle import matmul as OM
+    from oracle import quantize as OQ
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    M = N = K = 4096
+    rows = 4096
+    a32, b32 = synth.fp8_blockwise_raw(M, N, K, 204, 205)
+    _log(f"[bench] cpu baseline: oracle on {rows} of {M} rows ...")
+    t0 = time.perf_counter()
+    a, sa = OQ.fp8_rowblock(a32[:rows])
+    b, sb = OQ.fp8_tile(b32)
+    y, T = OM.blockwise_fp8(a, b, sa, sb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    _log(f"[bench] cpu baseline: {dt:.2f} s -> {flops / dt / 1e12:.5f} TFLOP/s")
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"one full step ({rows}x4096x4096): oracle 1x128 and 128x128 quantizers + float64 "
+                  f"blockwise GEMM with its error-bound GEMM; {dt:.2f} s",
+        "seconds": round(dt, 3),
+    }
+
+
+# --------------------------------------------------------------- suite ---
+
+def run_suite(args):
+    torch, bsq = _gpu_setup()
+    import numpy as np
+    import synth
+
+    dev = torch.device("cuda:0")
+    out_path = args.out
+    os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
+    rows = []
+
+    def time_launches(fn, n_iter, rotate=1):
+        for i in range(3):
+            fn(i % rotate)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(n_iter):
+            fn(i % rotate)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n_iter  # ms
+
+    def emit(row):
+        rows.append(row)
+        _log("[suite] " + json.dumps(row))
+        with open(out_path, "a") as f:
+            f.write(json.dumps(row) + "\n")
+
+    def hbm_row(name, workload, ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2), "bytes": int(nbytes),
+              "GB/s": round(gbs, 1), "pct_hbm": round(100 * gbs / PEAK_HBM_GBS, 1)})
+
+    def mfma_row(name, workload, ms, flops, peak):
+        tf = flops / (ms * 1e-3) / 1e12
+        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2), "flops": flops,
+              "TFLOP/s": round(tf, 1), "pct_peak": round(100 * tf / peak, 1)})
+
+    open(out_path, "w").close()
+    # ---- FP8 quantizers (rotating 8 input sets of 64 MB so the 256 MB cache cannot serve them)
+    for (R, C) in [(4096, 4096)]:
+        xs = [torch.randn(R, C, device=dev) for _ in range(8)]
+        codes = torch.empty(R, C, dtype=torch.uint8, device=dev)
+        sc = torch.empty(R, C // 128, dtype=torch.float32, device=dev)
+        ms = time_launches(lambda i: bsq.bsq_quant_fp8_rowblock(xs[i], codes, sc, 128), 40, 8)
+        hbm_row("quant_fp8_rowblock 1x128", f"{R}x{C} f32", ms, R * C * 5 + R * C // 128 * 4)
+        st = torch.empty(R // 128, C // 128, dtype=torch.float32, device=dev)
+        ms = time_launches(lambda i: bsq.bsq_quant_fp8_tile(xs[i], codes, st, 128, 128), 40, 8)
+        hbm_row("quant_fp8_tile 128x128", f"{R}x{C} f32", ms, R * C * 5 + st.numel() * 4)
+        del xs
+    # ---- FP8 GEMM sweep
+    for (M, N, K) in [(256, 512, 512)] + list(synth.FP8_SWEEP) + [(65536, 4096, 4096)]:
+        a = torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev)
+        b = torch.randint(0, 126, (N, K), dtype=torch.uint8, device=dev)
+        sa = torch.rand(M, K // 128, device=dev)
+        sb = torch.rand(N // 128, K // 128, device=dev)
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        n_it = 20 if M * N * K < 2 ** 38 else 5
+        ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(a, b, sa, sb, y), n_it)
+        mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} g128 f32 out", ms, 2 * M * N * K, PEAK_FP8_TFLOPS)
+        del a, b, sa, sb, y
+    # ---- INT8 per-channel
+    B, Din, Dout = 2048, 4096, 4096
+    x = torch.randn(B, Din, device=dev)
+    w = 0.02 * torch.randn(Din, Dout, device=dev)
+    xq = torch.empty(B, Din, dtype=torch.int8, device=dev)
+    xsc = torch.empty(B, device=dev)
+    wq = torch.empty(Din, Dout, dtype=torch.int8, device=dev)
+    wsc = torch.empty(Dout, device=dev)
+    wqT = torch.empty(Dout, Din, dtype=torch.int8, device=dev)
+    yi = torch.empty(B, Dout, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_int8_quant_rows(x, xq, xsc), 40)
+    hbm_row("int8_quant_rows", f"{B}x{Din} f32", ms, B * Din * 5 + B * 4)
+    ms = time_launches(lambda i: bsq.bsq_int8_quant_cols(w, wq, wsc, None), 40)
+    hbm_row("int8_quant_cols", f"{Din}x{Dout} f32 (w_q only)", ms, Din * Dout * 5 + Dout * 4)
+    ms = time_launches(lambda i: bsq.bsq_int8_quant_cols(w, wq, wsc, wqT), 40)
+    hbm_row("int8_quant_cols+T", f"{Din}x{Dout} f32 (w_q and w_qT)", ms, Din * Dout * 6 + Dout * 4)
+    ms = time_launches(lambda i: bsq.bsq_int8_matmul(xq, wqT, xsc, wsc, yi), 20)
+    mfma_row("gemm_int8", f"{B}x{Dout}x{Din} i32 acc, f32 epilogue", ms, 2 * B * Din * Dout, PEAK_INT8_TOPS)
+    del x, w, xq, wq, wqT, yi
+    # ---- MXFP8 batched scaled_matmul
+    Bt, M, N, K = 8, 2048, 2048, 4096
+    lhs32 = torch.randn(Bt * M, K, device=dev)
+    lq = torch.empty(Bt * M, K, dtype=torch.uint8, device=dev)
+    ls = torch.empty(Bt * M, K // 32, dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_quant_mx(lhs32, lq, ls, axis=1, code_dtype=bsq.BSQ_E4M3), 20)
+    hbm_row("quant_mx rows e4m3", f"{Bt * M}x{K} f32", ms, Bt * M * K * 5 + Bt * M * K // 32)
+    rq = lq.clone()
+    sa = torch.randint(124, 131, (Bt, M, K // 32), dtype=torch.uint8, device=dev)
+    sb = torch.randint(124, 131, (Bt, N, K // 32), dtype=torch.uint8, device=dev)
+    ym = torch.empty(Bt, M, N, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_scaled_matmul(lq.view(Bt, M, K), rq.view(Bt, N, K), sa, sb, ym,
+                                                       lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3,
+                                                       scale_dtype=bsq.BSQ_E8M0), 10)
+    mfma_row("gemm_mx_batched", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/32 f32 out", ms, 2 * Bt * M * N * K,
+             PEAK_FP8_TFLOPS)
+    del lhs32, lq, ls, rq, ym
+    # ---- MXFP8 backward
+    M, N, K = 8192, 4096, 4096
+    dY = torch.randn(M, N, device=dev).to(torch.bfloat16)
+    W = torch.randn(N, K, device=dev).to(torch.bfloat16)
+    X = torch.randn(M, K, device=dev).to(torch.bfloat16)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty(bsq.bsq_mxfp8_backward_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_mxfp8_backward(dY, W, X, dX, dW, wsb), 10)
+    mfma_row("mxfp8_backward (4 quant + 2 GEMM)", f"dY {M}x{N}, W {N}x{K}, X {M}x{K} e5m2 bf16 out", ms,
+             2 * 2 * M * N * K, PEAK_FP8_TFLOPS)
+    codes = torch.empty(N, M, dtype=torch.uint8, device=dev)
+    scs = torch.empty(N, M // 32, dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_quant_mx(dY, codes, scs, axis=0, code_dtype=bsq.BSQ_E5M2), 20)
+    hbm_row("quant_mx cols^T e5m2", f"{M}x{N} bf16", ms, M * N * 3 + M * N // 32)
+    _log(f"[suite] wrote {len(rows)} rows to {out_path}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--suite", action="store_true")
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "suite.jsonl"))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library's path runs on a single MI355X and has no "
+              "multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.suite:
+        run_suite(args)
+    else:
+        run_main(args)
+
+
+if __name__ == "__main__":
+    main()

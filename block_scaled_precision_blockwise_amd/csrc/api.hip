@@ -1,0 +1,414 @@
+// The C ABI of libbsq (declared in include/bsq.h): argument validation on
+// the host, then kernel launches on the caller's stream.
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "gemm.h"
+#include "quant.h"
+
+namespace bsq {
+
+namespace {
+thread_local std::string g_last_error;
+std::mutex g_dev_mu;
+std::vector<int> g_dev_state;  // per device: 0 unknown, 1 gfx950, 2 other
+}  // namespace
+
+bsq_status fail(bsq_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+bsq_status ok() {
+  g_last_error.clear();
+  return BSQ_OK;
+}
+
+bsq_status require_gfx950() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(BSQ_ERR_DEVICE, "no HIP device available");
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (size_t(dev) >= g_dev_state.size()) g_dev_state.resize(size_t(dev) + 1, 0);
+  if (g_dev_state[size_t(dev)] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(BSQ_ERR_DEVICE, "hipGetDeviceProperties failed");
+    }
+    g_dev_state[size_t(dev)] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (g_dev_state[size_t(dev)] != 1) return fail(BSQ_ERR_DEVICE, "the current device is not gfx950");
+  return BSQ_OK;
+}
+
+bsq_status launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BSQ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace bsq
+
+using namespace bsq;
+
+namespace {
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool is_fp8(int d) { return d == BSQ_E4M3 || d == BSQ_E5M2; }
+bool known_dtype(int d) { return d >= BSQ_F32 && d <= BSQ_I32; }
+
+// Shared tail of every call: the device check comes after the host-side
+// argument checks, so argument errors are reported without a GPU.
+#define BSQ_DEVICE()                                 \
+  do {                                               \
+    bsq_status _s = ::bsq::require_gfx950();         \
+    if (_s != BSQ_OK) return _s;                     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* bsq_version(void) { return "0.1.0"; }
+
+const char* bsq_status_string(int status) {
+  switch (status) {
+    case BSQ_OK: return "ok";
+    case BSQ_ERR_NULL: return "null pointer";
+    case BSQ_ERR_SHAPE: return "invalid shape";
+    case BSQ_ERR_DTYPE: return "invalid dtype";
+    case BSQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case BSQ_ERR_ALIGN: return "misaligned pointer";
+    case BSQ_ERR_DEVICE: return "no gfx950 device";
+    case BSQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsq_last_error(void) { return g_last_error.c_str(); }
+
+bsq_status bsq_device_check(void) {
+  const bsq_status s = require_gfx950();
+  return s == BSQ_OK ? ok() : s;
+}
+
+// ------------------------------------------------------------ quantizers --
+
+bsq_status bsq_quant_fp8_rowblock(int64_t rows, int64_t cols, int64_t group, const float* src,
+                                  uint8_t* codes, float* scales, void* stream) {
+  BSQ_CHECK(rows >= 0 && cols >= 0 && group > 0, BSQ_ERR_SHAPE, "negative size or group <= 0");
+  BSQ_CHECK(cols % group == 0, BSQ_ERR_SHAPE, "cols must be a multiple of group");
+  BSQ_CHECK(group == 32 || group == 64 || group == 128 || group == 256, BSQ_ERR_UNSUPPORTED,
+            "group must be 32, 64, 128 or 256");
+  if (rows == 0 || cols == 0) return ok();
+  BSQ_CHECK_PTR(src);
+  BSQ_CHECK_PTR(codes);
+  BSQ_CHECK_PTR(scales);
+  BSQ_DEVICE();
+  return launch_fp8_rowblock(rows, cols, group, src, codes, scales, as_stream(stream));
+}
+
+bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64_t group_c,
+                              const float* src, uint8_t* codes, float* scales, void* stream) {
+  BSQ_CHECK(rows >= 0 && cols >= 0 && group_r > 0 && group_c > 0, BSQ_ERR_SHAPE,
+            "negative size or group <= 0");
+  BSQ_CHECK(rows % group_r == 0 && cols % group_c == 0, BSQ_ERR_SHAPE,
+            "rows and cols must be multiples of the tile");
+  BSQ_CHECK(group_r == 128 && group_c == 128, BSQ_ERR_UNSUPPORTED, "tile must be 128 x 128");
+  if (rows == 0 || cols == 0) return ok();
+  BSQ_CHECK_PTR(src);
+  BSQ_CHECK_PTR(codes);
+  BSQ_CHECK_PTR(scales);
+  BSQ_DEVICE();
+  return launch_fp8_tile128(rows, cols, src, codes, scales, as_stream(stream));
+}
+
+bsq_status bsq_quant_mx(int64_t rows, int64_t cols, int axis, const void* src, int src_dtype,
+                        uint8_t* codes, int code_dtype, uint8_t* scales, void* stream) {
+  BSQ_CHECK(rows >= 0 && cols >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(axis == 0 || axis == 1, BSQ_ERR_SHAPE, "axis must be 0 or 1");
+  BSQ_CHECK(known_dtype(src_dtype) && known_dtype(code_dtype), BSQ_ERR_DTYPE, "unknown dtype");
+  BSQ_CHECK(src_dtype == BSQ_F32 || src_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
+            "src_dtype must be F32 or BF16");
+  BSQ_CHECK(is_fp8(code_dtype), BSQ_ERR_UNSUPPORTED, "code_dtype must be E4M3 or E5M2");
+  if (axis == 1) {
+    BSQ_CHECK(cols % 32 == 0, BSQ_ERR_SHAPE, "cols must be a multiple of 32 (axis 1)");
+  } else {
+    BSQ_CHECK(rows % 32 == 0 && cols % 32 == 0, BSQ_ERR_SHAPE,
+              "rows and cols must be multiples of 32 (axis 0)");
+  }
+  if (rows == 0 || cols == 0) return ok();
+  BSQ_CHECK_PTR(src);
+  BSQ_CHECK_PTR(codes);
+  BSQ_CHECK(scales != nullptr, BSQ_ERR_NULL, "scales is NULL");
+  BSQ_DEVICE();
+  return launch_mx(rows, cols, axis, src, src_dtype == BSQ_BF16, codes, code_dtype == BSQ_E5M2,
+                   scales, as_stream(stream));
+}
+
+bsq_status bsq_int8_quant_rows(int64_t B, int64_t D, const float* x, int8_t* x_q, float* x_s,
+                               void* stream) {
+  BSQ_CHECK(B >= 0 && D >= 0, BSQ_ERR_SHAPE, "negative size");
+  if (B == 0) return ok();
+  BSQ_CHECK_PTR(x_s);
+  if (D > 0) {
+    BSQ_CHECK_PTR(x);
+    BSQ_CHECK_PTR(x_q);
+  }
+  BSQ_DEVICE();
+  return launch_int8_rows(B, D, x, x_q, x_s, as_stream(stream));
+}
+
+bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* w_q,
+                               float* w_s, int8_t* w_qT, void* stream) {
+  BSQ_CHECK(D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
+  if (D_out == 0) return ok();
+  BSQ_CHECK_PTR(w_s);
+  if (D_in > 0) {
+    BSQ_CHECK_PTR(w);
+    BSQ_CHECK_PTR(w_q);
+    if (w_qT != nullptr) BSQ_CHECK(aligned16(w_qT), BSQ_ERR_ALIGN, "w_qT is not 16-byte aligned");
+  }
+  BSQ_DEVICE();
+  return launch_int8_cols(D_in, D_out, w, w_q, w_s, D_in > 0 ? w_qT : nullptr, as_stream(stream));
+}
+
+// --------------------------------------------------------------- matmuls --
+
+bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t group_n,
+                                    int64_t group_k, const uint8_t* a, const uint8_t* b,
+                                    const float* a_scales, const float* b_scales, void* out,
+                                    int out_dtype, void* stream) {
+  BSQ_CHECK(M >= 0 && N >= 0 && K >= 0 && group_n > 0 && group_k > 0, BSQ_ERR_SHAPE,
+            "negative size or group <= 0");
+  BSQ_CHECK(N % group_n == 0 && K % group_k == 0, BSQ_ERR_SHAPE,
+            "N and K must be multiples of group_n and group_k");
+  BSQ_CHECK(known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown out_dtype");
+  BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
+            "out_dtype must be F32 or BF16");
+  BSQ_CHECK(group_k == 128 && (group_n == 128 || group_n == 1), BSQ_ERR_UNSUPPORTED,
+            "this build runs group_k 128 with group_n 1 or 128");
+  BSQ_CHECK(N % 16 == 0, BSQ_ERR_UNSUPPORTED, "N must be a multiple of 16");
+  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30),
+            BSQ_ERR_UNSUPPORTED, "extent too large");
+  if (M == 0 || N == 0) return ok();
+  BSQ_CHECK_PTR(out);
+  if (K > 0) {
+    BSQ_CHECK_PTR(a);
+    BSQ_CHECK_PTR(b);
+    BSQ_CHECK(a_scales != nullptr && b_scales != nullptr, BSQ_ERR_NULL, "scales are NULL");
+  }
+  BSQ_DEVICE();
+  GemmLaunch L{};
+  L.mode = MODE_FP8G;
+  L.batch = 1;
+  L.M = M; L.N = N; L.K = K;
+  L.A = a; L.B = b; L.SA = a_scales; L.SB = b_scales;
+  L.out = out;
+  L.out_bf16 = out_dtype == BSQ_BF16;
+  L.gn1 = group_n == 1;
+  return launch_gemm(L, as_stream(stream));
+}
+
+bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t K_a,
+                             int64_t K_b, const void* lhs, int lhs_dtype, const void* rhs,
+                             int rhs_dtype, const void* lhs_scales, const void* rhs_scales,
+                             int scale_dtype, void* out, int out_dtype, void* stream) {
+  BSQ_CHECK(B >= 0 && M >= 0 && N >= 0 && K >= 0 && K_a >= 0 && K_b >= 0, BSQ_ERR_SHAPE,
+            "negative size");
+  BSQ_CHECK(K_a > 0 && K_b > 0 && K % K_a == 0 && K % K_b == 0, BSQ_ERR_SHAPE,
+            "K must be a multiple of K_a and of K_b");
+  BSQ_CHECK(known_dtype(lhs_dtype) && known_dtype(rhs_dtype) && known_dtype(scale_dtype) &&
+                known_dtype(out_dtype),
+            BSQ_ERR_DTYPE, "unknown dtype");
+  BSQ_CHECK(is_fp8(lhs_dtype) && is_fp8(rhs_dtype), BSQ_ERR_UNSUPPORTED,
+            "operands must be E4M3 or E5M2");
+  BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
+            "out_dtype must be F32 or BF16");
+  BSQ_CHECK(K % 128 == 0 && N % 16 == 0, BSQ_ERR_UNSUPPORTED,
+            "this build needs K % 128 == 0 and N % 16 == 0");
+  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30),
+            BSQ_ERR_UNSUPPORTED, "extent too large");
+  GemmLaunch L{};
+  if (scale_dtype == BSQ_E8M0) {
+    BSQ_CHECK(K_a == K / 32 && K_b == K / 32, BSQ_ERR_UNSUPPORTED, "E8M0 scales need block 32");
+    L.mode = MODE_MX;
+  } else if (scale_dtype == BSQ_F32) {
+    BSQ_CHECK(K_a == K / 128 && K_b == K / 128, BSQ_ERR_UNSUPPORTED, "F32 scales need block 128");
+    BSQ_CHECK(lhs_dtype == BSQ_E4M3 && rhs_dtype == BSQ_E4M3, BSQ_ERR_UNSUPPORTED,
+              "F32-scaled operands must be E4M3");
+    L.mode = MODE_FP8G;
+    L.gn1 = true;
+  } else {
+    return fail(BSQ_ERR_UNSUPPORTED, "scale_dtype must be E8M0 or F32");
+  }
+  if (B == 0 || M == 0 || N == 0) return ok();
+  BSQ_CHECK_PTR(out);
+  if (K > 0) {
+    BSQ_CHECK_PTR(lhs);
+    BSQ_CHECK_PTR(rhs);
+    BSQ_CHECK(lhs_scales != nullptr && rhs_scales != nullptr, BSQ_ERR_NULL, "scales are NULL");
+    if (scale_dtype == BSQ_E8M0)
+      BSQ_CHECK((reinterpret_cast<uintptr_t>(lhs_scales) & 3) == 0 &&
+                    (reinterpret_cast<uintptr_t>(rhs_scales) & 3) == 0,
+                BSQ_ERR_ALIGN, "scales must be 4-byte aligned");
+  }
+  BSQ_DEVICE();
+  L.batch = B;
+  L.M = M; L.N = N; L.K = K;
+  L.A = lhs; L.B = rhs; L.SA = lhs_scales; L.SB = rhs_scales;
+  L.out = out;
+  L.out_bf16 = out_dtype == BSQ_BF16;
+  L.fa_e5m2 = lhs_dtype == BSQ_E5M2;
+  L.fb_e5m2 = rhs_dtype == BSQ_E5M2;
+  return launch_gemm(L, as_stream(stream));
+}
+
+bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t* x_q,
+                           const int8_t* w_qT, const float* x_s, const float* w_s, float* y,
+                           int32_t* acc, void* stream) {
+  BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30) && D_in <= (int64_t(1) << 30),
+            BSQ_ERR_UNSUPPORTED, "extent too large");
+  if (B == 0 || D_out == 0) return ok();
+  BSQ_CHECK_PTR(y);
+  BSQ_CHECK(x_s != nullptr && w_s != nullptr, BSQ_ERR_NULL, "scales are NULL");
+  if (D_in > 0) {
+    BSQ_CHECK(x_q != nullptr && w_qT != nullptr, BSQ_ERR_NULL, "codes are NULL");
+  }
+  if (acc != nullptr) BSQ_CHECK(aligned16(acc), BSQ_ERR_ALIGN, "acc is not 16-byte aligned");
+  BSQ_DEVICE();
+  const bool mfma = D_in % 128 == 0 && D_out % 16 == 0 && aligned16(x_q) && aligned16(w_qT) &&
+                    aligned16(w_s) && D_in > 0;
+  if (!mfma)
+    return launch_int8_matmul_small(B, D_in, D_out, x_q, w_qT, x_s, w_s, y, acc, as_stream(stream));
+  GemmLaunch L{};
+  L.mode = MODE_I8;
+  L.batch = 1;
+  L.M = B; L.N = D_out; L.K = D_in;
+  L.A = x_q; L.B = w_qT; L.SA = x_s; L.SB = w_s;
+  L.out = y;
+  L.acc_out = acc;
+  return launch_gemm(L, as_stream(stream));
+}
+
+size_t bsq_int8_workspace_bytes(int64_t D_in, int64_t D_out) {
+  if (D_in <= 0 || D_out <= 0) return 0;
+  return size_t((D_in * D_out + 255) / 256 * 256);
+}
+
+bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, const float* x,
+                                       const float* w, int8_t* w_q, float* w_s, int8_t* x_q,
+                                       float* x_s, float* y, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(workspace_bytes >= bsq_int8_workspace_bytes(D_in, D_out), BSQ_ERR_SHAPE,
+            "workspace too small");
+  if (D_in > 0 && D_out > 0) BSQ_CHECK_PTR(workspace);
+  bsq_status s = bsq_int8_quant_rows(B, D_in, x, x_q, x_s, stream);
+  if (s != BSQ_OK) return s;
+  int8_t* wqT = static_cast<int8_t*>(workspace);
+  s = bsq_int8_quant_cols(D_in, D_out, w, w_q, w_s, D_in > 0 ? wqT : nullptr, stream);
+  if (s != BSQ_OK) return s;
+  return bsq_int8_matmul(B, D_in, D_out, x_q, wqT, x_s, w_s, y, nullptr, stream);
+}
+
+// MXFP8 backward: four MX quantizations into the workspace, then two
+// scaled GEMMs on K-contiguous operands.
+namespace {
+struct BwdLayout {
+  size_t dyn_codes, dyn_scales, wt_codes, wt_scales, dyt_codes, dyt_scales, xt_codes, xt_scales,
+      total;
+};
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
+  BwdLayout L{};
+  size_t o = 0;
+  auto take = [&o](size_t bytes) {
+    const size_t at = o;
+    o += up256(bytes);
+    return at;
+  };
+  L.dyn_codes = take(size_t(M * N));        // dY blocked along N: [M, N]
+  L.dyn_scales = take(size_t(M * (N / 32)));
+  L.wt_codes = take(size_t(K * N));         // W blocked along N, transposed: [K, N]
+  L.wt_scales = take(size_t(K * (N / 32)));
+  L.dyt_codes = take(size_t(N * M));        // dY blocked along M, transposed: [N, M]
+  L.dyt_scales = take(size_t(N * (M / 32)));
+  L.xt_codes = take(size_t(K * M));         // X blocked along M, transposed: [K, M]
+  L.xt_scales = take(size_t(K * (M / 32)));
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t bsq_mxfp8_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return bwd_layout(M, N, K).total;
+}
+
+bsq_status bsq_mxfp8_backward(int64_t M, int64_t N, int64_t K, const void* dY, const void* W,
+                              const void* X, int code_dtype, int out_dtype, void* dX, void* dW,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  BSQ_CHECK(M >= 0 && N >= 0 && K >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(known_dtype(code_dtype) && known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown dtype");
+  BSQ_CHECK(is_fp8(code_dtype), BSQ_ERR_UNSUPPORTED, "code_dtype must be E4M3 or E5M2");
+  BSQ_CHECK(out_dtype == BSQ_BF16 || out_dtype == BSQ_F32, BSQ_ERR_UNSUPPORTED,
+            "out_dtype must be BF16 or F32");
+  BSQ_CHECK(M % 128 == 0 && N % 128 == 0 && K % 128 == 0, BSQ_ERR_UNSUPPORTED,
+            "M, N and K must be multiples of 128");
+  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30),
+            BSQ_ERR_UNSUPPORTED, "extent too large");
+  const BwdLayout lay = bwd_layout(M, N, K);
+  BSQ_CHECK(workspace_bytes >= lay.total, BSQ_ERR_SHAPE, "workspace too small");
+  if (K == 0 || (M == 0 && N == 0)) return ok();  // both outputs are empty
+  if (M > 0) BSQ_CHECK_PTR(dX);
+  if (N > 0) BSQ_CHECK_PTR(dW);
+  if (M > 0 && N > 0) {
+    BSQ_CHECK_PTR(dY);
+    BSQ_CHECK_PTR(W);
+    BSQ_CHECK_PTR(X);
+    BSQ_CHECK_PTR(workspace);
+  }
+  BSQ_DEVICE();
+  hipStream_t st = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const bool e5 = code_dtype == BSQ_E5M2;
+  bsq_status s;
+  s = launch_mx(M, N, 1, dY, true, ws + lay.dyn_codes, e5, ws + lay.dyn_scales, st);
+  if (s != BSQ_OK) return s;
+  s = launch_mx(N, K, 0, W, true, ws + lay.wt_codes, e5, ws + lay.wt_scales, st);
+  if (s != BSQ_OK) return s;
+  s = launch_mx(M, N, 0, dY, true, ws + lay.dyt_codes, e5, ws + lay.dyt_scales, st);
+  if (s != BSQ_OK) return s;
+  s = launch_mx(M, K, 0, X, true, ws + lay.xt_codes, e5, ws + lay.xt_scales, st);
+  if (s != BSQ_OK) return s;
+  GemmLaunch L{};
+  L.mode = MODE_MX;
+  L.batch = 1;
+  L.out_bf16 = out_dtype == BSQ_BF16;
+  L.fa_e5m2 = L.fb_e5m2 = e5;
+  // dX [M, K] = dY [M, N] . W^T-layout [K, N] (contract N)
+  L.M = M; L.N = K; L.K = N;
+  L.A = ws + lay.dyn_codes; L.SA = ws + lay.dyn_scales;
+  L.B = ws + lay.wt_codes; L.SB = ws + lay.wt_scales;
+  L.out = dX;
+  s = launch_gemm(L, st);
+  if (s != BSQ_OK) return s;
+  // dW [N, K] = dY^T-layout [N, M] . X^T-layout [K, M] (contract M)
+  L.M = N; L.N = K; L.K = M;
+  L.A = ws + lay.dyt_codes; L.SA = ws + lay.dyt_scales;
+  L.B = ws + lay.xt_codes; L.SB = ws + lay.xt_scales;
+  L.out = dW;
+  return launch_gemm(L, st);
+}
+
+}  // extern "C"

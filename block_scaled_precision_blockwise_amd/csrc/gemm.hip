@@ -1,0 +1,381 @@
+// Block-scaled GEMM for gfx950: out[m, n] = sum_k A[m, k] B[n, k] with the
+// scales of the three modes this library runs.
+//
+//   FP8G  E4M3 operands, float32 scales per 128-wide K-block: one
+//         v_mfma_f32_16x16x128_f8f6f4 per K-block (exactly one 128-group),
+//         then a VALU rescale-and-add of the block's partial into the
+//         float32 accumulator (block_scaled_mm: dot per K-block, times the
+//         two scales, summed over K-blocks).
+//   MX    E4M3/E5M2 operands, E8M0 scales per 32 elements: the scaled MFMA
+//         v_mfma_scale_f32_16x16x128_f8f6f4 applies both scales in the
+//         matrix core and accumulates directly (scaled_matmul with mxfp8).
+//   I8    int8 operands, v_mfma_i32_16x16x64_i8 into int32 accumulators,
+//         float32 epilogue float(a) * (s_x * s_w) (int8 per-channel).
+//
+// Both operands are K-contiguous ("TN").  A workgroup of 8 waves owns a
+// 256 x 256 output tile and walks K in steps of 128; each step's A and B
+// tiles (32 KiB each) are double-buffered in LDS with a 16-byte-chunk XOR
+// swizzle so the fragment reads are free of bank conflicts.  Wave (wm, wn)
+// owns rows 64*wm..+64 and columns 128*wn..+128: 4 x 8 blocks of 16 x 16.
+//
+// Fragment layout (measured on gfx950): for the 16x16x128 f8 MFMA a lane
+// l supplies 32 bytes of row l % 16: K [16g, 16g+16) in bytes 0..15 and K
+// [64+16g, 64+16g+16) in bytes 16..31, g = l / 16; its E8M0 scale covers
+// K [32g, 32g+32).  The two 16x16x64 i8 MFMAs take the same two halves.
+// The result lane l holds column l % 16 of rows 4*(l/16) .. +3.  The MFMA's
+// first operand is the B fragment, so a lane's four results are four
+// consecutive n of one m: one 16-byte store, one A scale per lane.
+#include "common.h"
+#include "gemm.h"
+
+#include <type_traits>
+
+namespace bsq {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int THREADS = 512;
+
+struct GemmArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  const void* SA;
+  const void* SB;
+  void* out;
+  int32_t* acc_out;
+  int M, N, K;
+  int64_t sA, sB, sSA, sSB, sC;  // batch strides in elements of each array
+};
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int off0, int off1) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + off0);
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + off1);
+  v8i r;
+  r[0] = int(lo.x); r[1] = int(lo.y); r[2] = int(lo.z); r[3] = int(lo.w);
+  r[4] = int(hi.x); r[5] = int(hi.y); r[6] = int(hi.z); r[7] = int(hi.w);
+  return r;
+}
+
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
+__global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
+  __shared__ uint32_t lds_sa[2][BM];
+  __shared__ uint32_t lds_sb[2][BN];
+  __shared__ uint32_t lds_dummy[64];
+
+  const int tid = threadIdx.x;
+  const int batch = blockIdx.z;
+  const int m0 = blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nk = K / BK;
+
+  const uint8_t* A = p.A + int64_t(batch) * p.sA;
+  const uint8_t* B = p.B + int64_t(batch) * p.sB;
+
+  // ---- global -> LDS: direct 16-byte loads (global_load_lds_dwordx4).
+  // Lane i of a wave fills LDS bytes [16 i, 16 i + 16) of the wave's 1 KiB
+  // slice, i.e. row (wave_row0 + i / 8), physical chunk i % 8; it fetches
+  // the logical chunk that the XOR swizzle stores there.  Each wave moves
+  // 4 slices of A and 4 of B per K-step (rows 8w + 64 s .. + 8).
+  const int w = tid >> 6, lane = tid & 63;
+  const int lrow = 8 * w + (lane >> 3);  // + 64 s
+  const int lphys = lane & 7;
+  const int llog = lphys ^ (lrow & 7);
+  const uint8_t* gA[4];
+  const uint8_t* gB[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = lrow + 64 * s;
+    gA[s] = A + int64_t(min(m0 + r, M - 1)) * K + 16 * llog;
+    gB[s] = B + int64_t(min(n0 + r, N - 1)) * K + 16 * llog;
+  }
+  auto gload = [&](int ks, int st) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int slice = (8 * w + 64 * s) * BK;  // wave-uniform LDS byte offset
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(gA[s] + int64_t(ks) * BK),
+          (__attribute__((address_space(3))) void*)(&lds_a[st][slice]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(gB[s] + int64_t(ks) * BK),
+          (__attribute__((address_space(3))) void*)(&lds_b[st][slice]), 16, 0, 0);
+    }
+  };
+
+  // ---- per-step scales, staged through one register into LDS.
+  // FP8G: thread t < 256 loads the A scale of row t; B scales per row (GN1)
+  // or per 128-row group.  MX: 4 E8M0 bytes per row per step.  Threads
+  // without a scale to move read a valid word and write a dummy LDS slot,
+  // so the loop body has no divergent branches.
+  const uint32_t* sptr = nullptr;
+  uint32_t* sdst[2] = {&lds_dummy[tid & 63], &lds_dummy[tid & 63]};
+  if (MODE == MODE_FP8G) {
+    const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + int64_t(batch) * p.sSA;
+    const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + int64_t(batch) * p.sSB;
+    sptr = SA;
+    if (tid < 256) {
+      sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
+    } else if (GN1) {
+      sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
+    } else if (tid - 256 < 2 && n0 + 128 * (tid - 256) < N) {
+      sptr = SB + int64_t(n0 / 128 + (tid - 256)) * nk;
+    }
+    if (tid < 256 || GN1 || (tid - 256 < 2 && n0 + 128 * (tid - 256) < N)) {
+      sdst[0] = tid < 256 ? &lds_sa[0][tid] : &lds_sb[0][tid - 256];
+      sdst[1] = tid < 256 ? &lds_sa[1][tid] : &lds_sb[1][tid - 256];
+    }
+  } else if (MODE == MODE_MX) {
+    const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + p.sSA / 4 * batch;
+    const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + p.sSB / 4 * batch;
+    if (tid < 256) sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
+    else sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
+    sdst[0] = tid < 256 ? &lds_sa[0][tid] : &lds_sb[0][tid - 256];
+    sdst[1] = tid < 256 ? &lds_sa[1][tid] : &lds_sb[1][tid - 256];
+  }
+
+  // ---- wave / lane roles in the MFMA loop
+  const int wm = w & 3, wn = w >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int swz = r16 & 7;
+  const int c0 = 16 * (g ^ swz), c1 = 16 * ((g + 4) ^ swz);
+
+  typedef typename std::conditional<MODE == MODE_I8, v4i, v4f>::type acc_t;
+  acc_t acc[8][4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
+
+  constexpr bool kScales = MODE != MODE_I8;
+  gload(0, 0);
+  if (kScales) *sdst[0] = sptr[0];
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
+  __syncthreads();
+
+  for (int ks = 0; ks < nk; ++ks) {
+    const int st = ks & 1;
+    // the next step's tiles and scales; the last step reloads its own tile
+    // into the idle buffer so that the body has no branch
+    const int kn = min(ks + 1, nk - 1);
+    gload(kn, st ^ 1);
+    uint32_t s_next = 0;
+    if (kScales) s_next = sptr[kn];
+
+    const uint8_t* ta = lds_a[st];
+    const uint8_t* tb = lds_b[st];
+    v8i q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wm + 16 * i + r16;
+      q[i] = lds_frag(ta, row * BK + c0, row * BK + c1);
+    }
+    float sa[4];
+    int qa[4];
+    float sbg = 0.f;
+    if (MODE == MODE_FP8G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i] = __uint_as_float(lds_sa[st][64 * wm + 16 * i + r16]);
+      if (!GN1) sbg = __uint_as_float(lds_sb[st][wn]);
+    } else if (MODE == MODE_MX) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qa[i] = int((lds_sa[st][64 * wm + 16 * i + r16] >> (8 * g)) & 0xFFu);
+    }
+    v8i pb = lds_frag(tb, (128 * wn + r16) * BK + c0, (128 * wn + r16) * BK + c1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rowb = 128 * wn + 16 * j + r16;
+      v8i pn;
+      if (j < 7) pn = lds_frag(tb, (rowb + 16) * BK + c0, (rowb + 16) * BK + c1);
+      if (MODE == MODE_FP8G) {
+        float sb4[4];
+        if (GN1) {
+          const uint4 v = *reinterpret_cast<const uint4*>(&lds_sb[st][128 * wn + 16 * j + 4 * g]);
+          sb4[0] = __uint_as_float(v.x); sb4[1] = __uint_as_float(v.y);
+          sb4[2] = __uint_as_float(v.z); sb4[3] = __uint_as_float(v.w);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4f zero = {0.f, 0.f, 0.f, 0.f};
+          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], zero, 0, 0, 0, 0, 0, 0);
+          if (GN1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(d[r], sa[i] * sb4[r], acc[j][i][r]);
+          } else {
+            const float sc = sa[i] * sbg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(d[r], sc, acc[j][i][r]);
+          }
+        }
+      } else if (MODE == MODE_MX) {
+        const int qb = int((lds_sb[st][rowb] >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], acc[j][i], FB, FA, 0,
+                                                                       qb, 0, qa[i]);
+      } else {
+        const v4i plo = {pb[0], pb[1], pb[2], pb[3]};
+        const v4i phi = {pb[4], pb[5], pb[6], pb[7]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4i qlo = {q[i][0], q[i][1], q[i][2], q[i][3]};
+          const v4i qhi = {q[i][4], q[i][5], q[i][6], q[i][7]};
+          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(plo, qlo, acc[j][i], 0, 0, 0);
+          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(phi, qhi, acc[j][i], 0, 0, 0);
+        }
+      }
+      if (j < 7) pb = pn;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    if (kScales) *sdst[st ^ 1] = s_next;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 64 * wm + 16 * i + r16;
+    if (m >= M) continue;
+    float xs = 0.f;
+    if (MODE == MODE_I8) xs = static_cast<const float*>(p.SA)[int64_t(batch) * p.sSA + m];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + 128 * wn + 16 * j + 4 * g;
+      if (n >= N) continue;
+      const int64_t o = int64_t(batch) * p.sC + int64_t(m) * N + n;
+      float y[4];
+      if (MODE == MODE_I8) {
+        const float4 ws = *reinterpret_cast<const float4*>(static_cast<const float*>(p.SB) +
+                                                           int64_t(batch) * p.sSB + n);
+        const float wsv[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = float(acc[j][i][r]) * (xs * wsv[r]);
+        if (p.acc_out != nullptr)
+          *reinterpret_cast<int4*>(p.acc_out + o) =
+              make_int4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = float(acc[j][i][r]);
+      }
+      if (OUT_BF16) {
+        const uint32_t lo = encode_bf16(y[0]) | (encode_bf16(y[1]) << 16);
+        const uint32_t hi = encode_bf16(y[2]) | (encode_bf16(y[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(y[0], y[1], y[2], y[3]);
+      }
+    }
+  }
+}
+
+__global__ void k_zero_bytes(uint32_t* __restrict__ p, int64_t n_words) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n_words; i += int64_t(gridDim.x) * 256)
+    p[i] = 0u;
+}
+
+bsq_status zero_fill(void* p, int64_t bytes, hipStream_t st) {
+  if (bytes == 0) return ok();
+  const int64_t words = bytes / 4;
+  int64_t grid = (words + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(k_zero_bytes, unsigned(grid), 256, 0, st, static_cast<uint32_t*>(p), words);
+  return launch_status("zero fill");
+}
+
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
+bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
+  dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
+  hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1>), grid, THREADS, 0, st, a);
+  return launch_status("gemm");
+}
+
+__global__ void __launch_bounds__(256) k_int8_small(const int8_t* __restrict__ xq,
+                                                    const int8_t* __restrict__ wqT,
+                                                    const float* __restrict__ xs,
+                                                    const float* __restrict__ ws,
+                                                    float* __restrict__ y, int32_t* __restrict__ acc,
+                                                    int64_t Bn, int64_t D_in, int64_t D_out) {
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= Bn * D_out) return;
+  const int64_t b = idx / D_out, j = idx % D_out;
+  const int8_t* xr = xq + b * D_in;
+  const int8_t* wr = wqT + j * D_in;
+  int32_t a = 0;
+  for (int64_t i = 0; i < D_in; ++i) a += int32_t(xr[i]) * int32_t(wr[i]);
+  y[idx] = float(a) * (xs[b] * ws[j]);
+  if (acc != nullptr) acc[idx] = a;
+}
+
+}  // namespace
+
+bsq_status launch_int8_matmul_small(int64_t B, int64_t D_in, int64_t D_out, const int8_t* xq,
+                                    const int8_t* wqT, const float* xs, const float* ws, float* y,
+                                    int32_t* acc, hipStream_t st) {
+  const int64_t n = B * D_out;
+  if (n == 0) return ok();
+  hipLaunchKernelGGL(k_int8_small, unsigned((n + 255) / 256), 256, 0, st, xq, wqT, xs, ws, y, acc,
+                     B, D_in, D_out);
+  return launch_status("int8_matmul (small shapes)");
+}
+
+bsq_status launch_gemm(const GemmLaunch& L, hipStream_t st) {
+  const int64_t out_elem = L.out_bf16 ? 2 : 4;
+  if (L.batch == 0 || L.M == 0 || L.N == 0) return ok();
+  if (L.K == 0) {
+    bsq_status s = zero_fill(L.out, L.batch * L.M * L.N * out_elem, st);
+    if (s == BSQ_OK && L.acc_out) s = zero_fill(L.acc_out, L.batch * L.M * L.N * 4, st);
+    return s;
+  }
+  GemmArgs a;
+  a.A = static_cast<const uint8_t*>(L.A);
+  a.B = static_cast<const uint8_t*>(L.B);
+  a.SA = L.SA;
+  a.SB = L.SB;
+  a.out = L.out;
+  a.acc_out = L.acc_out;
+  a.M = int(L.M);
+  a.N = int(L.N);
+  a.K = int(L.K);
+  a.sA = L.M * L.K;
+  a.sB = L.N * L.K;
+  a.sC = L.M * L.N;
+  switch (L.mode) {
+    case MODE_FP8G:
+      a.sSA = L.M * (L.K / 128);
+      a.sSB = (L.gn1 ? L.N : L.N / 128) * (L.K / 128);
+      if (L.gn1) return L.out_bf16 ? run<MODE_FP8G, 1, 0, 0, 1>(a, int(L.batch), st)
+                                   : run<MODE_FP8G, 0, 0, 0, 1>(a, int(L.batch), st);
+      return L.out_bf16 ? run<MODE_FP8G, 1, 0, 0, 0>(a, int(L.batch), st)
+                        : run<MODE_FP8G, 0, 0, 0, 0>(a, int(L.batch), st);
+    case MODE_MX: {
+      a.sSA = L.M * (L.K / 32);
+      a.sSB = L.N * (L.K / 32);
+      const int sel = (L.fa_e5m2 ? 1 : 0) | (L.fb_e5m2 ? 2 : 0) | (L.out_bf16 ? 4 : 0);
+      switch (sel) {
+        case 0: return run<MODE_MX, 0, 0, 0, 0>(a, int(L.batch), st);
+        case 1: return run<MODE_MX, 0, 1, 0, 0>(a, int(L.batch), st);
+        case 2: return run<MODE_MX, 0, 0, 1, 0>(a, int(L.batch), st);
+        case 3: return run<MODE_MX, 0, 1, 1, 0>(a, int(L.batch), st);
+        case 4: return run<MODE_MX, 1, 0, 0, 0>(a, int(L.batch), st);
+        case 5: return run<MODE_MX, 1, 1, 0, 0>(a, int(L.batch), st);
+        case 6: return run<MODE_MX, 1, 0, 1, 0>(a, int(L.batch), st);
+        default: return run<MODE_MX, 1, 1, 1, 0>(a, int(L.batch), st);
+      }
+    }
+    case MODE_I8:
+      a.sSA = L.M;
+      a.sSB = L.N;
+      return run<MODE_I8, 0, 0, 0, 0>(a, int(L.batch), st);
+  }
+  return fail(BSQ_ERR_UNSUPPORTED, "unknown gemm mode");
+}
+
+}  // namespace bsq

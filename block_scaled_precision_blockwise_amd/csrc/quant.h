@@ -1,0 +1,19 @@
+// Launchers of the quantizer kernels (arguments already validated).
+#pragma once
+
+#include "common.h"
+
+namespace bsq {
+
+bsq_status launch_fp8_rowblock(int64_t rows, int64_t cols, int64_t group, const float* src,
+                               uint8_t* codes, float* scales, hipStream_t st);
+bsq_status launch_fp8_tile128(int64_t rows, int64_t cols, const float* src, uint8_t* codes,
+                              float* scales, hipStream_t st);
+bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool src_bf16,
+                     uint8_t* codes, bool e5m2, uint8_t* scales, hipStream_t st);
+bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, float* xs,
+                            hipStream_t st);
+bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* wq, float* ws,
+                            int8_t* wqT, hipStream_t st);
+
+}  // namespace bsq

@@ -1,0 +1,573 @@
+// Quantizer kernels: float values -> fp8 / int8 codes plus scales.
+//
+// All of them are bound by HBM: one streaming read of the input, one write
+// of the codes.  Blocks are reduced inside a wavefront with cross-lane
+// shuffles; per-element division is a true IEEE float32 division (the
+// pages divide by the scale), never a reciprocal multiply.
+#include "common.h"
+#include "quant.h"
+
+namespace bsq {
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+
+__device__ __forceinline__ float amax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WIDTH));
+  return v;
+}
+
+// fp32 block scale of the block_scaled_mm recipe: max(amax / 448, 1e-10).
+__device__ __forceinline__ float fp8_block_scale(float amax) {
+  return fmaxf(amax / kE4M3Max, scale_floor());
+}
+
+__device__ __forceinline__ uint32_t quant4_e4m3(float4 v, float s) {
+  auto q = [s](float x) {
+    const float y = fminf(fmaxf(x / s, -kE4M3Max), kE4M3Max);
+    return encode_e4m3(y);
+  };
+  return q(v.x) | (q(v.y) << 8) | (q(v.z) << 16) | (q(v.w) << 24);
+}
+
+// ------------------------------------------------ fp8 1 x G row blocks ----
+// One float4 per lane, G/4 lanes per block; a workgroup handles U chunks of
+// 256 float4 per grid-stride step, all loads issued before any use.
+template <int G, int U>
+__global__ void __launch_bounds__(256) k_fp8_rowblock(const float4* __restrict__ src,
+                                                      uint32_t* __restrict__ codes,
+                                                      float* __restrict__ scales, int64_t n4) {
+  constexpr int LPB = G / 4;
+  const int64_t chunk = int64_t(256) * U;
+  for (int64_t base = int64_t(blockIdx.x) * chunk; base < n4; base += int64_t(gridDim.x) * chunk) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t f = base + u * 256 + threadIdx.x;
+      v[u] = f < n4 ? ldnt(src + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t f = base + u * 256 + threadIdx.x;
+      const float amax = group_max<LPB>(amax4(v[u]));
+      const float s = fp8_block_scale(amax);
+      if (f < n4) {
+        codes[f] = quant4_e4m3(v[u], s);
+        if ((threadIdx.x % LPB) == 0) scales[f / LPB] = s;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------ fp8 128 x 128 tiles ----
+// One workgroup per tile; each thread holds 64 values (16 float4) of the
+// tile in registers between the reduction and the encode.
+__global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ src,
+                                                     uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scales, int64_t cols) {
+  __shared__ float wmax[4];
+  const int tx = threadIdx.x;
+  const int c4 = tx & 31;
+  const int r0 = tx >> 5;
+  const int64_t row0 = int64_t(blockIdx.y) * 128;
+  const int64_t col0 = int64_t(blockIdx.x) * 128 + 4 * c4;
+  float4 v[16];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4* p = reinterpret_cast<const float4*>(src + (row0 + r0 + 8 * i) * cols + col0);
+    v[i] = ldnt(p);
+    m = fmaxf(m, amax4(v[i]));
+  }
+  m = group_max<64>(m);
+  if ((tx & 63) == 0) wmax[tx >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = fp8_block_scale(amax);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t* q = reinterpret_cast<uint32_t*>(codes + (row0 + r0 + 8 * i) * cols + col0);
+    *q = quant4_e4m3(v[i], s);
+  }
+  if (tx == 0) scales[int64_t(blockIdx.y) * gridDim.x + blockIdx.x] = s;
+}
+
+// ------------------------------------------------------------ MX (e8m0) --
+// Exponent of the block scale: the smallest E with max(amax, 1e-10) <=
+// fmax * 2^E, read off the float32 fields.  fmax = 1.75 * 2^EMAX for both
+// formats (448 = 1.75 * 2^8, 57344 = 1.75 * 2^15).
+template <int EMAX>
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const uint32_t u = __float_as_uint(fmaxf(amax, scale_floor()));
+  const int e = int((u >> 23) & 0xFFu) - 127;
+  const int E = e - EMAX + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return min(max(E, -127), 127);
+}
+
+template <int CODE>  // 0 = e4m3, 1 = e5m2
+__device__ __forceinline__ uint32_t mx_encode(float x, int E) {
+  const float y = ldexpf(x, -E);
+  if (CODE == 0) return encode_e4m3(fminf(fmaxf(y, -kE4M3Max), kE4M3Max));
+  return encode_e5m2(fminf(fmaxf(y, -kE5M2Max), kE5M2Max));
+}
+
+// Loads 8 consecutive source values as float (from f32 or bf16).
+template <int SRC_BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float (&x)[8]) {
+  if (SRC_BF16) {
+    const uint4 w = ldnt(
+        reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem));
+    const uint32_t p[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = decode_bf16(p[i] & 0xFFFFu);
+      x[2 * i + 1] = decode_bf16(p[i] >> 16);
+    }
+  } else {
+    const float4* f = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    const float4 a = ldnt(f);
+    const float4 b = ldnt(f + 1);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
+// Blocks of 32 along rows (axis = 1): 4 lanes per block, 8 values each.
+template <int SRC_BF16, int CODE, int U>
+__global__ void __launch_bounds__(256) k_mx_rows(const void* __restrict__ src,
+                                                 uint2* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, int64_t n8) {
+  constexpr int EMAX = CODE == 0 ? 8 : 15;
+  const int64_t chunk = int64_t(256) * U;
+  for (int64_t base = int64_t(blockIdx.x) * chunk; base < n8; base += int64_t(gridDim.x) * chunk) {
+    float x[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t f = base + u * 256 + threadIdx.x;
+      if (f < n8) {
+        load8<SRC_BF16>(src, f * 8, x[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[u][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t f = base + u * 256 + threadIdx.x;
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[u][i]));
+      m = group_max<4>(m);
+      const int E = mx_exponent<EMAX>(m);
+      if (f < n8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo |= mx_encode<CODE>(x[u][i], E) << (8 * i);
+          hi |= mx_encode<CODE>(x[u][4 + i], E) << (8 * i);
+        }
+        codes[f] = make_uint2(lo, hi);
+        if ((threadIdx.x & 3) == 0) scales[f >> 2] = uint8_t(E + 127);
+      }
+    }
+  }
+}
+
+// Blocks of 32 down columns (axis = 0), output transposed.  A workgroup
+// takes a 64 x 64 tile through LDS; thread t writes 16 codes of output row
+// (input column) t / 4, two threads per 32-block.
+template <int SRC_BF16, int CODE>
+__global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales, int64_t rows,
+                                                   int64_t cols) {
+  constexpr int EMAX = CODE == 0 ? 8 : 15;
+  __shared__ float tile[64][65];
+  const int tx = threadIdx.x;
+  const int64_t r0 = int64_t(blockIdx.y) * 64;
+  const int64_t c0 = int64_t(blockIdx.x) * 64;
+  // load: 64 rows x 64 cols, 8 values per thread-step, 2 steps
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int idx = tx + 256 * s;  // 0..511: row idx / 8, col group idx % 8
+    const int r = idx >> 3, cg = (idx & 7) * 8;
+    float x[8];
+    if (r0 + r < rows && c0 + cg < cols) {
+      load8<SRC_BF16>(src, (r0 + r) * cols + c0 + cg, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[r][cg + i] = x[i];
+  }
+  __syncthreads();
+  const int oc = tx >> 2, seg = tx & 3;
+  float x[16];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = tile[16 * seg + i][oc];
+    m = fmaxf(m, fabsf(x[i]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  const int E = mx_exponent<EMAX>(m);
+  const int64_t orow = c0 + oc;
+  const int64_t ocol = r0 + 16 * seg;
+  if (orow < cols && ocol < rows) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[q] |= mx_encode<CODE>(x[4 * q + i], E) << (8 * i);
+    }
+    *reinterpret_cast<uint4*>(codes + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
+    if ((seg & 1) == 0) scales[orow * (rows / 32) + (ocol >> 5)] = uint8_t(E + 127);
+  }
+}
+
+// ------------------------------------------------------ int8 per-channel --
+
+__device__ __forceinline__ float int8_scale(float amax) {
+  return amax == 0.f ? 1.0f : amax / 127.0f;
+}
+
+__device__ __forceinline__ int32_t int8_code(float x, float s) {
+  const float r = __builtin_rintf(x / s);
+  return int32_t(fminf(fmaxf(r, -127.f), 127.f));
+}
+
+__device__ __forceinline__ uint32_t int8_pack4(float4 v, float s) {
+  return (uint32_t(int8_code(v.x, s)) & 0xFFu) | ((uint32_t(int8_code(v.y, s)) & 0xFFu) << 8) |
+         ((uint32_t(int8_code(v.z, s)) & 0xFFu) << 16) | ((uint32_t(int8_code(v.w, s)) & 0xFFu) << 24);
+}
+
+template <int N>
+__device__ __forceinline__ float block_max(float m, float* red) {
+  m = group_max<64>(m);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+// One workgroup per row, D % 4 == 0, the row held in registers (V float4
+// per thread).
+template <int V>
+__global__ void __launch_bounds__(256) k_int8_rows_vec(const float* __restrict__ x,
+                                                       uint32_t* __restrict__ xq,
+                                                       float* __restrict__ xs, int64_t D) {
+  __shared__ float red[4];
+  const int64_t d4 = D / 4;
+  const float4* row = reinterpret_cast<const float4*>(x + int64_t(blockIdx.x) * D);
+  float4 v[V];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int64_t c = threadIdx.x + 256 * i;
+    v[i] = c < d4 ? ldnt(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    m = fmaxf(m, amax4(v[i]));
+  }
+  const float s = int8_scale(block_max<4>(m, red));
+  uint32_t* out = xq + int64_t(blockIdx.x) * d4;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const int64_t c = threadIdx.x + 256 * i;
+    if (c < d4) out[c] = int8_pack4(v[i], s);
+  }
+  if (threadIdx.x == 0) xs[blockIdx.x] = s;
+}
+
+// Any D: two passes over the row (the second from cache).
+__global__ void __launch_bounds__(256) k_int8_rows_any(const float* __restrict__ x,
+                                                       int8_t* __restrict__ xq,
+                                                       float* __restrict__ xs, int64_t D) {
+  __shared__ float red[4];
+  const float* row = x + int64_t(blockIdx.x) * D;
+  float m = 0.f;
+  for (int64_t c = threadIdx.x; c < D; c += 256) m = fmaxf(m, fabsf(row[c]));
+  const float s = int8_scale(block_max<4>(m, red));
+  int8_t* out = xq + int64_t(blockIdx.x) * D;
+  for (int64_t c = threadIdx.x; c < D; c += 256) out[c] = int8_t(int8_code(row[c], s));
+  if (threadIdx.x == 0) xs[blockIdx.x] = s;
+}
+
+// Column maxima of w[D_in, D_out] by atomic max on the float bits (all
+// values are >= 0, so the unsigned order is the float order).  A workgroup
+// covers up to 256 columns and `rows_per_wg` rows.
+__global__ void __launch_bounds__(256) k_int8_colmax(const float* __restrict__ w,
+                                                     uint32_t* __restrict__ cmax, int64_t D_in,
+                                                     int64_t D_out, int rows_per_wg) {
+  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t r_begin = int64_t(blockIdx.y) * rows_per_wg;
+  const int64_t r_end = min(r_begin + rows_per_wg, D_in);
+  // 256 threads walk 256 consecutive columns one row at a time
+  float m = 0.f;
+  if (c < D_out) {
+    for (int64_t r = r_begin; r < r_end; ++r) m = fmaxf(m, fabsf(w[r * D_out + c]));
+    atomicMax(cmax + c, __float_as_uint(m));
+  }
+}
+
+// Vector variant: D_out % 4 == 0; 64 float4 columns x 4 row phases.
+__global__ void __launch_bounds__(256) k_int8_colmax_vec(const float4* __restrict__ w,
+                                                         uint32_t* __restrict__ cmax,
+                                                         int64_t D_in, int64_t d4,
+                                                         int rows_per_wg) {
+  __shared__ float4 part[4][64];
+  const int tx = threadIdx.x;
+  const int cx = tx & 63, ph = tx >> 6;
+  const int64_t c = int64_t(blockIdx.x) * 64 + cx;
+  const int64_t r_begin = int64_t(blockIdx.y) * rows_per_wg;
+  const int64_t r_end = min(r_begin + rows_per_wg, D_in);
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < d4) {
+    int64_t r = r_begin + ph;
+    for (; r + 12 < r_end; r += 16) {
+      const float4 a = ldnt(w + r * d4 + c);
+      const float4 b = ldnt(w + (r + 4) * d4 + c);
+      const float4 e = ldnt(w + (r + 8) * d4 + c);
+      const float4 f = ldnt(w + (r + 12) * d4 + c);
+      m.x = fmaxf(fmaxf(m.x, fmaxf(fabsf(a.x), fabsf(b.x))), fmaxf(fabsf(e.x), fabsf(f.x)));
+      m.y = fmaxf(fmaxf(m.y, fmaxf(fabsf(a.y), fabsf(b.y))), fmaxf(fabsf(e.y), fabsf(f.y)));
+      m.z = fmaxf(fmaxf(m.z, fmaxf(fabsf(a.z), fabsf(b.z))), fmaxf(fabsf(e.z), fabsf(f.z)));
+      m.w = fmaxf(fmaxf(m.w, fmaxf(fabsf(a.w), fabsf(b.w))), fmaxf(fabsf(e.w), fabsf(f.w)));
+    }
+    for (; r < r_end; r += 4) {
+      const float4 a = ldnt(w + r * d4 + c);
+      m.x = fmaxf(m.x, fabsf(a.x));
+      m.y = fmaxf(m.y, fabsf(a.y));
+      m.z = fmaxf(m.z, fabsf(a.z));
+      m.w = fmaxf(m.w, fabsf(a.w));
+    }
+  }
+  part[ph][cx] = m;
+  __syncthreads();
+  if (ph == 0 && c < d4) {
+#pragma unroll
+    for (int p = 1; p < 4; ++p) {
+      const float4 o = part[p][cx];
+      m.x = fmaxf(m.x, o.x);
+      m.y = fmaxf(m.y, o.y);
+      m.z = fmaxf(m.z, o.z);
+      m.w = fmaxf(m.w, o.w);
+    }
+    uint32_t* dst = cmax + 4 * c;
+    atomicMax(dst + 0, __float_as_uint(m.x));
+    atomicMax(dst + 1, __float_as_uint(m.y));
+    atomicMax(dst + 2, __float_as_uint(m.z));
+    atomicMax(dst + 3, __float_as_uint(m.w));
+  }
+}
+
+__global__ void __launch_bounds__(256) k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256)
+    p[i] = v;
+}
+
+// Codes of w with the column scales derived from the column maxima; also
+// the transposed codes w_qT[D_out, D_in] when requested.  Tiles of 128 x
+// 128 (D_in x D_out) through LDS; any sizes (edges guarded).
+__global__ void __launch_bounds__(256) k_int8_cols_quant(const float* __restrict__ w,
+                                                         const uint32_t* __restrict__ cmax,
+                                                         int8_t* __restrict__ wq,
+                                                         int8_t* __restrict__ wqT, int64_t D_in,
+                                                         int64_t D_out) {
+  __shared__ uint8_t tq[128][128 + 16];
+  const int tx = threadIdx.x;
+  const int64_t i0 = int64_t(blockIdx.y) * 128;  // rows of w (D_in)
+  const int64_t j0 = int64_t(blockIdx.x) * 128;  // cols of w (D_out)
+  const int cx = tx & 31;                         // 4 columns each
+  const int rr = tx >> 5;                         // 8 row phases
+  const bool vec = (D_out % 4) == 0;
+  float s[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t j = j0 + 4 * cx + q;
+    s[q] = j < D_out ? int8_scale(__uint_as_float(cmax[j])) : 1.0f;
+  }
+  for (int k = 0; k < 16; ++k) {
+    const int r = rr + 8 * k;
+    const int64_t i = i0 + r;
+    const int64_t j = j0 + 4 * cx;
+    uint32_t packed = 0;
+    if (i < D_in) {
+      if (vec && j < D_out) {
+        const float4 v = ldnt(reinterpret_cast<const float4*>(w + i * D_out + j));
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) packed |= (uint32_t(int8_code(vv[q], s[q])) & 0xFFu) << (8 * q);
+        *reinterpret_cast<uint32_t*>(wq + i * D_out + j) = packed;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (j + q < D_out) {
+            const int32_t c = int8_code(w[i * D_out + j + q], s[q]);
+            wq[i * D_out + j + q] = int8_t(c);
+            packed |= (uint32_t(c) & 0xFFu) << (8 * q);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tq[4 * cx + q][r] = uint8_t(packed >> (8 * q));
+  }
+  if (wqT == nullptr) return;
+  __syncthreads();
+  // 128 output rows (j) x 128 bytes (i): thread writes 64 bytes of one row
+  const int oj = tx >> 1, half = tx & 1;
+  const int64_t j = j0 + oj;
+  if (j >= D_out) return;
+  const int64_t ib = i0 + 64 * half;
+  int8_t* dst = wqT + j * D_in + ib;
+  if ((D_in % 16) == 0 && ib + 64 <= D_in) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint8_t* srow = &tq[oj][64 * half + 16 * q];
+      uint4 pk;
+      pk.x = srow[0] | (srow[1] << 8) | (srow[2] << 16) | (uint32_t(srow[3]) << 24);
+      pk.y = srow[4] | (srow[5] << 8) | (srow[6] << 16) | (uint32_t(srow[7]) << 24);
+      pk.z = srow[8] | (srow[9] << 8) | (srow[10] << 16) | (uint32_t(srow[11]) << 24);
+      pk.w = srow[12] | (srow[13] << 8) | (srow[14] << 16) | (uint32_t(srow[15]) << 24);
+      *reinterpret_cast<uint4*>(dst + 16 * q) = pk;
+    }
+  } else {
+    for (int q = 0; q < 64 && ib + q < D_in; ++q) dst[q] = int8_t(tq[oj][64 * half + q]);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_int8_col_scales(const uint32_t* __restrict__ cmax,
+                                                         float* __restrict__ ws, int64_t n) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j < n) ws[j] = int8_scale(__uint_as_float(cmax[j]));
+}
+
+int grid_for(int64_t work_items, int per_wg) {
+  int64_t g = (work_items + per_wg - 1) / per_wg;
+  // a few waves of workgroups per CU is enough for a streaming kernel
+  const int64_t cap = 256 * 16;
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return int(g);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ launchers --
+
+bsq_status launch_fp8_rowblock(int64_t rows, int64_t cols, int64_t group, const float* src,
+                               uint8_t* codes, float* scales, hipStream_t st) {
+  const int64_t n4 = rows * cols / 4;
+  if (n4 == 0) return ok();
+  constexpr int U = 4;
+  const int grid = grid_for(n4, 256 * U);
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  uint32_t* c4 = reinterpret_cast<uint32_t*>(codes);
+  switch (group) {
+    case 32: hipLaunchKernelGGL((k_fp8_rowblock<32, U>), grid, 256, 0, st, s4, c4, scales, n4); break;
+    case 64: hipLaunchKernelGGL((k_fp8_rowblock<64, U>), grid, 256, 0, st, s4, c4, scales, n4); break;
+    case 128: hipLaunchKernelGGL((k_fp8_rowblock<128, U>), grid, 256, 0, st, s4, c4, scales, n4); break;
+    case 256: hipLaunchKernelGGL((k_fp8_rowblock<256, U>), grid, 256, 0, st, s4, c4, scales, n4); break;
+    default: return fail(BSQ_ERR_UNSUPPORTED, "fp8 row-block group must be 32, 64, 128 or 256");
+  }
+  return launch_status("quant_fp8_rowblock");
+}
+
+bsq_status launch_fp8_tile128(int64_t rows, int64_t cols, const float* src, uint8_t* codes,
+                              float* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return ok();
+  dim3 grid(unsigned(cols / 128), unsigned(rows / 128));
+  hipLaunchKernelGGL(k_fp8_tile128, grid, 256, 0, st, src, codes, scales, cols);
+  return launch_status("quant_fp8_tile");
+}
+
+bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool src_bf16,
+                     uint8_t* codes, bool e5m2, uint8_t* scales, hipStream_t st) {
+  if (rows == 0 || cols == 0) return ok();
+  if (axis == 1) {
+    const int64_t n8 = rows * cols / 8;
+    constexpr int U = 2;
+    const int grid = grid_for(n8, 256 * U);
+    uint2* c8 = reinterpret_cast<uint2*>(codes);
+#define BSQ_MXR(B, C) hipLaunchKernelGGL((k_mx_rows<B, C, U>), grid, 256, 0, st, src, c8, scales, n8)
+    if (src_bf16) {
+      if (e5m2) BSQ_MXR(1, 1); else BSQ_MXR(1, 0);
+    } else {
+      if (e5m2) BSQ_MXR(0, 1); else BSQ_MXR(0, 0);
+    }
+#undef BSQ_MXR
+  } else {
+    dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64));
+#define BSQ_MXC(B, C) hipLaunchKernelGGL((k_mx_cols_t<B, C>), grid, 256, 0, st, src, codes, scales, rows, cols)
+    if (src_bf16) {
+      if (e5m2) BSQ_MXC(1, 1); else BSQ_MXC(1, 0);
+    } else {
+      if (e5m2) BSQ_MXC(0, 1); else BSQ_MXC(0, 0);
+    }
+#undef BSQ_MXC
+  }
+  return launch_status("quant_mx");
+}
+
+bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, float* xs,
+                            hipStream_t st) {
+  if (B == 0) return ok();
+  if (D == 0) {
+    // an empty row is all zero: scale 1
+    hipLaunchKernelGGL(k_fill_u32, grid_for(B, 256), 256, 0, st, reinterpret_cast<uint32_t*>(xs), B,
+                       0x3F800000u);
+    return launch_status("int8_quant_rows");
+  }
+  const int64_t d4 = D / 4;
+  uint32_t* q4 = reinterpret_cast<uint32_t*>(xq);
+  const unsigned g = unsigned(B);
+  if (D % 4 == 0 && d4 <= 256 * 16) {
+    if (d4 <= 256) hipLaunchKernelGGL(k_int8_rows_vec<1>, g, 256, 0, st, x, q4, xs, D);
+    else if (d4 <= 512) hipLaunchKernelGGL(k_int8_rows_vec<2>, g, 256, 0, st, x, q4, xs, D);
+    else if (d4 <= 1024) hipLaunchKernelGGL(k_int8_rows_vec<4>, g, 256, 0, st, x, q4, xs, D);
+    else if (d4 <= 2048) hipLaunchKernelGGL(k_int8_rows_vec<8>, g, 256, 0, st, x, q4, xs, D);
+    else hipLaunchKernelGGL(k_int8_rows_vec<16>, g, 256, 0, st, x, q4, xs, D);
+  } else {
+    hipLaunchKernelGGL(k_int8_rows_any, g, 256, 0, st, x, xq, xs, D);
+  }
+  return launch_status("int8_quant_rows");
+}
+
+bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* wq, float* ws,
+                            int8_t* wqT, hipStream_t st) {
+  if (D_out == 0) return ok();
+  uint32_t* cmax = reinterpret_cast<uint32_t*>(ws);  // column maxima live in w_s until the end
+  hipLaunchKernelGGL(k_fill_u32, grid_for(D_out, 256), 256, 0, st, cmax, D_out, 0u);
+  if (D_in > 0) {
+    const int rows_per_wg = 64;
+    const unsigned gy = unsigned((D_in + rows_per_wg - 1) / rows_per_wg);
+    if (D_out % 4 == 0) {
+      const int64_t d4 = D_out / 4;
+      dim3 grid(unsigned((d4 + 63) / 64), gy);
+      hipLaunchKernelGGL(k_int8_colmax_vec, grid, 256, 0, st, reinterpret_cast<const float4*>(w),
+                         cmax, D_in, d4, rows_per_wg);
+    } else {
+      dim3 grid(unsigned((D_out + 255) / 256), gy);
+      hipLaunchKernelGGL(k_int8_colmax, grid, 256, 0, st, w, cmax, D_in, D_out, rows_per_wg);
+    }
+    dim3 grid(unsigned((D_out + 127) / 128), unsigned((D_in + 127) / 128));
+    hipLaunchKernelGGL(k_int8_cols_quant, grid, 256, 0, st, w, cmax, wq, wqT, D_in, D_out);
+  }
+  hipLaunchKernelGGL(k_int8_col_scales, unsigned((D_out + 255) / 256), 256, 0, st, cmax, ws, D_out);
+  return launch_status("int8_quant_cols");
+}
+
+}  // namespace bsq

@@ -1,0 +1,210 @@
+/*
+ * bsq.h - block-scaled quantized matmul for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Conventions shared by every call:
+ *
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or keeps a pointer after the call
+ *     returns.  Tensors are dense row-major; base addresses must be 16-byte
+ *     aligned.  Sizes are int64_t element counts.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Each call validates its arguments on the host, enqueues its kernels
+ *     on `stream` and returns without synchronising.  Kernel errors that
+ *     the launch itself reports are returned as BSQ_ERR_HIP.
+ *   - Every call returns a bsq_status.  On failure nothing has been
+ *     enqueued and bsq_last_error() (thread-local) describes the cause.
+ *   - A call with an empty extent (a zero size) is a valid no-op unless the
+ *     call's own rules say otherwise.
+ *   - Non-finite inputs give unspecified results (the pages state all
+ *     values are finite).
+ *   - Format names: E4M3 = OCP float8_e4m3fn, E5M2 = OCP float8_e5m2,
+ *     E8M0 = OCP float8_e8m0fnu (scale 2^(b-127)), BF16 = bfloat16.
+ *
+ * Citations name the web page and the part of it that defines the
+ * operation: "scaled_matmul" = jax.nn.scaled_matmul documentation;
+ * "block_scaled_mm" = atrex-bench operator #002; "int8 per-channel" =
+ * TensorTonic "Int8 Matmul with Per-Channel Scales"; "mxfp8 backward" =
+ * AWS Neuron NKI matmul_mxfp8_backward API reference.
+ */
+#ifndef BSQ_H
+#define BSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsq_status {
+  BSQ_OK = 0,
+  BSQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  BSQ_ERR_SHAPE = 2,       /* sizes negative, not divisible, or inconsistent */
+  BSQ_ERR_DTYPE = 3,       /* a format code outside the enum */
+  BSQ_ERR_UNSUPPORTED = 4, /* a valid combination this library does not run */
+  BSQ_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+  BSQ_ERR_DEVICE = 6,      /* no HIP device, or the current device is not gfx950 */
+  BSQ_ERR_HIP = 7          /* the HIP runtime reported an error */
+} bsq_status;
+
+typedef enum bsq_dtype {
+  BSQ_F32 = 0,
+  BSQ_BF16 = 1,
+  BSQ_E4M3 = 2,
+  BSQ_E5M2 = 3,
+  BSQ_E8M0 = 4,
+  BSQ_I8 = 5,
+  BSQ_I32 = 6
+} bsq_dtype;
+
+/* ---------------------------------------------------------------- misc -- */
+
+/* Library version string, e.g. "0.1.0". Static storage. */
+const char* bsq_version(void);
+/* Static description of a status code. */
+const char* bsq_status_string(int status);
+/* Thread-local message for the last failing call on this thread ("" if
+ * none).  Valid until the next call on the same thread. */
+const char* bsq_last_error(void);
+/* Checks that a HIP device is present and the current one is gfx950.
+ * Returns BSQ_OK or BSQ_ERR_DEVICE. */
+bsq_status bsq_device_check(void);
+
+/* ---------------------------------------------------------- quantizers -- */
+
+/* FP8 activation quantizer with 1 x `group` blocks along each row.
+ * block_scaled_mm, "Input Generation" (activation path): per block
+ * amax = max|x|, s = max(amax / 448, 1e-10) (float32), codes =
+ * e4m3fn(clamp(x / s, -448, 448)) with a true float32 division and
+ * round-to-nearest-even.
+ *   src    float32 [rows, cols]
+ *   codes  uint8   [rows, cols]          (E4M3 bytes, out)
+ *   scales float32 [rows, cols / group]  (out)
+ * Rules: cols % group == 0, group % 32 == 0 and group <= 1024; rows may be
+ * 0. */
+bsq_status bsq_quant_fp8_rowblock(int64_t rows, int64_t cols, int64_t group,
+                                  const float* src, uint8_t* codes, float* scales,
+                                  void* stream);
+
+/* FP8 weight quantizer with one scale per group_r x group_c tile.
+ * block_scaled_mm, "Input Generation" (weight path), with the tile
+ * maximum taken over absolute values (the page's weight path omits abs();
+ * the activation path and the workload description use it).
+ *   src    float32 [rows, cols]
+ *   codes  uint8   [rows, cols]                        (E4M3, out)
+ *   scales float32 [rows / group_r, cols / group_c]    (out)
+ * Rules: rows % group_r == 0, cols % group_c == 0; this build runs
+ * group_r == group_c == 128. */
+bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64_t group_c,
+                              const float* src, uint8_t* codes, float* scales, void* stream);
+
+/* MX quantizer: 32-element blocks with an E8M0 scale.
+ * scaled_matmul, Notes (mxfp8: e4m3fn or e5m2 codes, e8m0 scales, block
+ * 32); mxfp8 backward, Parameters (float8_dtype).  The pages do not state
+ * the scale rule; this library's: E = the smallest integer with
+ * max(amax, 1e-10) <= fmax * 2^E (fmax 448 for E4M3, 57344 for E5M2),
+ * scale byte E + 127, codes = fp8(x * 2^-E) rounded to nearest even.
+ *   axis = 1: blocks run along each row.  codes [rows, cols],
+ *             scales [rows, cols / 32].
+ *   axis = 0: blocks run down each column and the output is written
+ *             transposed: codes [cols, rows], scales [cols, rows / 32]
+ *             (the layout the backward products consume).
+ *   src_dtype  BSQ_F32 or BSQ_BF16;  code_dtype BSQ_E4M3 or BSQ_E5M2.
+ * Rules: the blocked extent is a multiple of 32; for axis = 0 both rows
+ * and cols are multiples of 32. */
+bsq_status bsq_quant_mx(int64_t rows, int64_t cols, int axis, const void* src, int src_dtype,
+                        uint8_t* codes, int code_dtype, uint8_t* scales, void* stream);
+
+/* INT8 per-channel quantizer for activations, one scale per row.
+ * int8 per-channel, scale and code formulas: s_b = max_i |x_bi| / 127
+ * (float32), s_b = 1 when the row is all zero, q = clip(round(x / s),
+ * -127, 127), round = nearest with ties to even.
+ *   x [B, D] float32 -> x_q [B, D] int8, x_s [B] float32. */
+bsq_status bsq_int8_quant_rows(int64_t B, int64_t D, const float* x, int8_t* x_q, float* x_s,
+                               void* stream);
+
+/* INT8 per-channel quantizer for weights, one scale per column.
+ * int8 per-channel, as above with the max over each column of w.
+ *   w    [D_in, D_out] float32
+ *   w_q  [D_in, D_out] int8 (w's layout, out)
+ *   w_s  [D_out] float32 (out)
+ *   w_qT [D_out, D_in] int8, the same codes transposed (K-contiguous, for
+ *        bsq_int8_matmul), or NULL to skip. */
+bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* w_q,
+                               float* w_s, int8_t* w_qT, void* stream);
+
+/* -------------------------------------------------------------- matmuls -- */
+
+/* block_scaled_mm: y[m, n] = sum over K-blocks kb of
+ *   a_scales[m, kb] * b_scales[n / group_n, kb] * sum_{k in kb} a[m,k] b[n,k]
+ * (block_scaled_mm, "Reference Implementation").
+ *   a        E4M3 [M, K]            b        E4M3 [N, K]  (both K-contiguous)
+ *   a_scales float32 [M, K / group_k]
+ *   b_scales float32 [N / group_n, K / group_k]
+ *   out      [M, N], out_dtype BSQ_F32 or BSQ_BF16 (nearest even)
+ * Rules: N % group_n == 0, K % group_k == 0; M >= 0 arbitrary.  This build
+ * runs group_k == 128 with group_n in {1, 128}; others -> UNSUPPORTED. */
+bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t group_n,
+                                    int64_t group_k, const uint8_t* a, const uint8_t* b,
+                                    const float* a_scales, const float* b_scales, void* out,
+                                    int out_dtype, void* stream);
+
+/* scaled_matmul: out[b, m, n] = sum_k lhs[b,m,k] lhs_scales[b,m,k/(K/K_a)]
+ *                                     rhs[b,n,k] rhs_scales[b,n,k/(K/K_b)]
+ * (scaled_matmul, "Mathematically" and Parameters; block size K / K_a).
+ *   lhs [B, M, K], rhs [B, N, K] codes (lhs_dtype / rhs_dtype E4M3 or E5M2)
+ *   lhs_scales [B, M, K_a], rhs_scales [B, N, K_b] of scale_dtype
+ *   out [B, M, N] of out_dtype (BSQ_F32, the page's default, or BSQ_BF16)
+ * Rules: K % K_a == 0 and K % K_b == 0 (else SHAPE).  This build runs
+ * scale_dtype E8M0 with block 32 (K_a == K_b == K / 32) and scale_dtype F32
+ * with block 128 (K_a == K_b == K / 128), K % 128 == 0; other valid
+ * combinations -> UNSUPPORTED. */
+bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t K_a,
+                             int64_t K_b, const void* lhs, int lhs_dtype, const void* rhs,
+                             int rhs_dtype, const void* lhs_scales, const void* rhs_scales,
+                             int scale_dtype, void* out, int out_dtype, void* stream);
+
+/* INT8 matmul with per-channel scales (int8 per-channel, output formula and
+ * Requirements): a[b, j] = sum_i x_q[b,i] w_q[i,j] accumulated in int32,
+ * y[b, j] = float32(a[b, j]) * (x_s[b] * w_s[j]) in float32.
+ *   x_q  [B, D_in] int8;  w_qT [D_out, D_in] int8 (w_q transposed, as
+ *   written by bsq_int8_quant_cols);  x_s [B], w_s [D_out] float32
+ *   y [B, D_out] float32 (out); acc [B, D_out] int32 (out) or NULL.
+ * Rules: D_in % 128 == 0 in this build (else UNSUPPORTED). */
+bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t* x_q,
+                           const int8_t* w_qT, const float* x_s, const float* w_s, float* y,
+                           int32_t* acc, void* stream);
+
+/* The whole int8 per-channel problem: quantize x by rows and w by
+ * columns, multiply in int8 with int32 sums, apply the float32 epilogue.
+ * Writes the five results the problem returns (w_q, w_scales, x_q,
+ * x_scales, y).  `workspace` holds the transposed weight codes: at least
+ * bsq_int8_workspace_bytes(D_in, D_out) bytes, 16-byte aligned. */
+size_t bsq_int8_workspace_bytes(int64_t D_in, int64_t D_out);
+bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, const float* x,
+                                       const float* w, int8_t* w_q, float* w_s, int8_t* x_q,
+                                       float* x_s, float* y, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* MXFP8 linear-layer backward (mxfp8 backward: forward Y = X W^T with X
+ * [M, K], W [N, K]; dX = dY W [M, K] contracting over N; dW = dY^T X [N, K]
+ * contracting over M; bf16 inputs quantized on the fly).
+ *   dY [M, N], W [N, K], X [M, K]: BSQ_BF16
+ *   code_dtype: BSQ_E5M2 (the page's default) or BSQ_E4M3
+ *   out_dtype:  BSQ_BF16 (the page's default) or BSQ_F32
+ *   dX [M, K], dW [N, K] (out)
+ * The MX blocks run along each product's contraction axis.  `workspace`
+ * receives the quantized operands: at least
+ * bsq_mxfp8_backward_workspace_bytes(M, N, K) bytes.
+ * Rules: M, N, K multiples of 128 (else UNSUPPORTED; negative -> SHAPE);
+ * a smaller workspace -> SHAPE. */
+size_t bsq_mxfp8_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+bsq_status bsq_mxfp8_backward(int64_t M, int64_t N, int64_t K, const void* dY, const void* W,
+                              const void* X, int code_dtype, int out_dtype, void* dX, void* dW,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSQ_H */

@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: libbsq.so loads, exports every function that
+include/bsq.h declares, and rejects invalid arguments on the host before it
+touches a device (each error path of the validation is forced here)."""
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_blockwise_amd as bsq
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bsq.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, DEVICE, HIP = range(8)
+A16 = 0x1000   # a 16-byte-aligned fake device address, never dereferenced
+A4 = 0x1004
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not bsq.is_built():
+        import __graft_entry__
+        __graft_entry__.build()
+    return bsq.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bsq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert bsq.bsq_version() == "0.1.0"
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.bsq_status_string(s)
+    assert L.bsq_status_string(99) == b"unknown status"
+
+
+def _expect(status, want, L):
+    assert status == want, (status, L.bsq_last_error())
+
+
+def test_fp8_rowblock_validation(L):
+    f = L.bsq_quant_fp8_rowblock
+    _expect(f(-1, 128, 128, A16, A16, A16, None), SHAPE, L)
+    _expect(f(4, 100, 128, A16, A16, A16, None), SHAPE, L)      # cols % group
+    _expect(f(4, 144, 48, A16, A16, A16, None), UNSUP, L)      # group 48
+    _expect(f(4, 128, 128, None, A16, A16, None), NULL, L)
+    _expect(f(4, 128, 128, A4, A16, A16, None), ALIGN, L)
+    _expect(f(0, 128, 128, None, None, None, None), OK, L)     # empty is a no-op
+    # valid arguments reach the device check
+    _expect(f(4, 128, 128, A16, A16, A16, None), DEVICE, L)
+    assert L.bsq_last_error()
+
+
+def test_fp8_tile_validation(L):
+    f = L.bsq_quant_fp8_tile
+    _expect(f(100, 128, 128, 128, A16, A16, A16, None), SHAPE, L)
+    _expect(f(128, 128, 64, 64, A16, A16, A16, None), UNSUP, L)
+    _expect(f(128, 128, 128, 128, A16, None, A16, None), NULL, L)
+
+
+def test_mx_validation(L):
+    f = L.bsq_quant_mx
+    _expect(f(4, 48, 1, A16, bsq.BSQ_F32, A16, bsq.BSQ_E4M3, A16, None), SHAPE, L)
+    _expect(f(48, 64, 0, A16, bsq.BSQ_F32, A16, bsq.BSQ_E4M3, A16, None), SHAPE, L)
+    _expect(f(4, 64, 2, A16, bsq.BSQ_F32, A16, bsq.BSQ_E4M3, A16, None), SHAPE, L)
+    _expect(f(4, 64, 1, A16, 17, A16, bsq.BSQ_E4M3, A16, None), DTYPE, L)
+    _expect(f(4, 64, 1, A16, bsq.BSQ_I8, A16, bsq.BSQ_E4M3, A16, None), UNSUP, L)
+    _expect(f(4, 64, 1, A16, bsq.BSQ_F32, A16, bsq.BSQ_F32, A16, None), UNSUP, L)
+
+
+def test_blockwise_validation(L):
+    f = L.bsq_blockwise_fp8_matmul
+    args = (A16, A16, A16, A16, A16, bsq.BSQ_F32, None)
+    _expect(f(16, 256, 200, 128, 128, *args), SHAPE, L)        # K % group_k
+    _expect(f(16, 200, 256, 128, 128, *args), SHAPE, L)        # N % group_n
+    _expect(f(16, 256, 256, 64, 128, *args), UNSUP, L)         # group_n 64
+    _expect(f(16, 256, 256, 128, 128, A16, A16, A16, A16, A16, bsq.BSQ_I8, None), UNSUP, L)
+    _expect(f(16, 256, 256, 128, 128, A16, A16, A16, A16, A16, 42, None), DTYPE, L)
+    _expect(f(0, 256, 256, 128, 128, None, None, None, None, None, bsq.BSQ_F32, None), OK, L)
+    _expect(f(16, 256, 256, 128, 128, A16, A16, A16, A16, None, bsq.BSQ_F32, None), NULL, L)
+    _expect(f(16, 256, 256, 128, 128, *args), DEVICE, L)
+
+
+def test_scaled_matmul_validation(L):
+    f = L.bsq_scaled_matmul
+    E4, E5, E8, F32 = bsq.BSQ_E4M3, bsq.BSQ_E5M2, bsq.BSQ_E8M0, bsq.BSQ_F32
+    # K % K_a != 0 is a shape error (the page's rule)
+    _expect(f(1, 8, 16, 128, 3, 4, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), SHAPE, L)
+    # valid but not run here: block 16 e8m0, or an int8 operand
+    _expect(f(1, 8, 16, 128, 8, 8, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
+    _expect(f(1, 8, 16, 128, 4, 4, A16, bsq.BSQ_I8, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
+    _expect(f(1, 8, 16, 128, 4, 4, A16, E4, A16, E5, A16, A16, E8, A16, F32, None), DEVICE, L)
+    _expect(f(1, 8, 16, 256, 2, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), DEVICE, L)
+    _expect(f(1, 8, 16, 256, 2, 2, A16, E5, A16, E4, A16, A16, F32, A16, F32, None), UNSUP, L)
+    _expect(f(1, 8, 16, 128, 4, 4, A16, E4, A16, E4, A4 + 1, A16, E8, A16, F32, None), ALIGN, L)
+
+
+def test_int8_validation(L):
+    _expect(L.bsq_int8_quant_rows(-2, 4, A16, A16, A16, None), SHAPE, L)
+    _expect(L.bsq_int8_quant_rows(2, 4, A16, A16, None, None), NULL, L)
+    _expect(L.bsq_int8_quant_cols(4, 2, A16, A16, A16, A4, None), ALIGN, L)
+    _expect(L.bsq_int8_matmul(2, 4, 3, A16, A16, None, A16, A16, None, None), NULL, L)
+    _expect(L.bsq_int8_matmul(2, 4, 3, A16, A16, A16, A16, A16, None, None), DEVICE, L)
+    need = L.bsq_int8_workspace_bytes(4096, 4096)
+    assert need >= 4096 * 4096
+    _expect(L.bsq_int8_per_channel_matmul(2, 4096, 4096, A16, A16, A16, A16, A16, A16, A16, A16,
+                                          need - 1, None), SHAPE, L)
+
+
+def test_backward_validation(L):
+    f = L.bsq_mxfp8_backward
+    need = L.bsq_mxfp8_backward_workspace_bytes(256, 256, 256)
+    assert need >= 4 * 256 * 256
+    E5, BF = bsq.BSQ_E5M2, bsq.BSQ_BF16
+    _expect(f(256, 256, 200, A16, A16, A16, E5, BF, A16, A16, A16, need, None), UNSUP, L)
+    _expect(f(256, 256, 256, A16, A16, A16, E5, BF, A16, A16, A16, need - 1, None), SHAPE, L)
+    _expect(f(256, 256, 256, A16, A16, A16, bsq.BSQ_I8, BF, A16, A16, A16, need, None), UNSUP, L)
+    _expect(f(256, 256, 256, A16, A16, A16, E5, BF, A16, A16, None, need, None), NULL, L)
+    _expect(f(256, 256, 256, A16, A16, A16, E5, BF, A16, A16, A16, need, None), DEVICE, L)
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    x = torch.zeros(4, 128)
+    with pytest.raises(ValueError):
+        bsq.bsq_quant_fp8_rowblock(x, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))

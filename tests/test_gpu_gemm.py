@@ -1,0 +1,377 @@
+"""GPU parity of the GEMMs against the CPU oracle, through the C ABI.
+
+Floating-point outputs: |y - y_ref| <= 1e-4 T with T = sum_k |a s_a b s_b|
+(plus 2^-8 |y_ref| for bf16 outputs) on operands drawn as the pages draw
+them (randn quantized by the recipe).  Operands of uniformly random fp8
+codes span the whole exponent range of the format; for those the bound adds
+the fp8 matrix core's measured group-of-8 truncation allowance
+(gpu_helpers.fp8_group_bound).  Integer sums: bit-exact.  Full-size shapes
+are checked on sampled rows (rows are independent in every product),
+including the first and last rows and rows at tile boundaries.
+"""
+import numpy as np
+import pytest
+
+import block_scaled_precision_blockwise_amd as bsq
+import synth
+from oracle import backward as OB
+from oracle import formats as OF
+from oracle import matmul as OM
+from oracle import quantize as OQ
+
+from gpu_helpers import (assert_bytes_equal, assert_within_T, assert_within_T_hw, empty, filled,
+                         fp8_group_bound, host, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _rows_sample(M, n=40, seed=0):
+    g = np.random.default_rng(seed)
+    base = {0, 1, M - 1, M // 2}
+    for t in (255, 256, 257, 511, 512):
+        if t < M:
+            base.add(t)
+    extra = g.choice(M, size=min(n, M), replace=False)
+    return np.array(sorted(base | set(int(v) for v in extra)))
+
+
+def _random_blockwise(M, N, K, seed):
+    """Uniformly random E4M3 codes and log-uniform scales (full range)."""
+    a = synth.random_fp8_codes((M, K), seed, "e4m3")
+    b = synth.random_fp8_codes((N, K), seed + 1, "e4m3")
+    sa = synth.random_f32_scales((M, K // 128), seed + 2)
+    sb = synth.random_f32_scales((N // 128, K // 128), seed + 3)
+    return a, b, sa, sb
+
+
+def _recipe_blockwise(M, N, K, seed):
+    """Operands as block_scaled_mm draws them: randn quantized with 1 x 128
+    activation scales and 128 x 128 weight scales (oracle quantizers)."""
+    a32, b32 = synth.fp8_blockwise_raw(M, N, K, seed, seed + 1)
+    a, sa = OQ.fp8_rowblock(a32)
+    b, sb = OQ.fp8_tile(b32)
+    return a, b, sa, sb
+
+
+def _blockwise_hw_bound(a, b, sa, sb):
+    A = np.abs(OF.decode(a, "e4m3")) * np.repeat(sa.astype(np.float64), 128, axis=1)
+    Bv = np.abs(OF.decode(b, "e4m3")) * np.repeat(np.repeat(sb.astype(np.float64), 128, axis=0), 128, axis=1)
+    return fp8_group_bound(A, Bv)
+
+
+def _run_blockwise(a, b, sa, sb, out_dtype=None, group_n=128):
+    torch = _torch()
+    M, N = a.shape[0], b.shape[0]
+    y = filled((M, N), out_dtype or torch.float32, float("nan"))
+    bsq.bsq_blockwise_fp8_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, group_n=group_n)
+    return y
+
+
+def test_blockwise_small_end_to_end():
+    """The small block_scaled_mm case end to end: GPU quantizers then GEMM."""
+    torch = _torch()
+    M, N, K = synth.FP8_TINY
+    say("blockwise end to end", M, N, K)
+    a32, b32 = synth.fp8_blockwise_raw(M, N, K, 0, 1)
+    aq = empty((M, K), torch.uint8)
+    bq = empty((N, K), torch.uint8)
+    sa = empty((M, K // 128), torch.float32)
+    sb = empty((N // 128, K // 128), torch.float32)
+    y = filled((M, N), torch.float32, float("nan"))
+    bsq.bsq_quant_fp8_rowblock(to_dev(a32), aq, sa, 128)
+    bsq.bsq_quant_fp8_tile(to_dev(b32), bq, sb, 128, 128)
+    bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y)
+    ra, rsa = OQ.fp8_rowblock(a32)
+    rb, rsb = OQ.fp8_tile(b32)
+    assert_bytes_equal(host(aq), ra, "a codes")
+    assert_bytes_equal(host(bq), rb, "b codes")
+    yr, T = OM.blockwise_fp8(ra, rb, rsa, rsb)
+    assert_within_T(host(y), yr, T, "y")
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (237, 4096, 4096), (349, 2048, 2048), (1, 128, 128), (300, 384, 640), (513, 256, 256),
+])
+def test_blockwise_full_compare(M, N, K):
+    say("blockwise full (recipe operands)", M, N, K)
+    a, b, sa, sb = _recipe_blockwise(M, N, K, 600 + M)
+    y = _run_blockwise(a, b, sa, sb)
+    yr, T = OM.blockwise_fp8(a, b, sa, sb)
+    assert_within_T(host(y), yr, T, "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(349, 2048, 2048), (300, 384, 640), (513, 256, 256)])
+def test_blockwise_full_range_codes(M, N, K):
+    say("blockwise full (random codes)", M, N, K)
+    a, b, sa, sb = _random_blockwise(M, N, K, 650 + M)
+    y = _run_blockwise(a, b, sa, sb)
+    yr, T = OM.blockwise_fp8(a, b, sa, sb)
+    assert_within_T_hw(host(y), yr, T, _blockwise_hw_bound(a, b, sa, sb), "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(3072, 4096, 4096), (4096, 4096, 4096), (1024, 2048, 2048),
+                                   (6918, 2048, 2048)])
+def test_blockwise_sweep_sampled(M, N, K):
+    say("blockwise sampled", M, N, K)
+    a, b, sa, sb = _random_blockwise(M, N, K, 700 + M)
+    y = host(_run_blockwise(a, b, sa, sb))
+    rows = _rows_sample(M, seed=M)
+    yr, T = OM.blockwise_fp8(a[rows], b, sa[rows], sb)
+    G = _blockwise_hw_bound(a[rows], b, sa[rows], sb)
+    assert_within_T_hw(y[rows], yr, T, G, "y rows")
+    assert np.all(np.isfinite(y)), "unwritten output"
+
+
+def test_blockwise_from_quantized_randn_full_size():
+    """The headline shape with operands from the recipe (randn quantized by
+    the GPU quantizers), checked on sampled rows."""
+    torch = _torch()
+    M = N = K = 4096
+    say("blockwise 4096^3 from randn")
+    a32, b32 = synth.fp8_blockwise_raw(M, N, K, 204, 205)
+    aq = empty((M, K), torch.uint8)
+    bq = empty((N, K), torch.uint8)
+    sa = empty((M, K // 128), torch.float32)
+    sb = empty((N // 128, K // 128), torch.float32)
+    y = filled((M, N), torch.float32, float("nan"))
+    bsq.bsq_quant_fp8_rowblock(to_dev(a32), aq, sa, 128)
+    bsq.bsq_quant_fp8_tile(to_dev(b32), bq, sb, 128, 128)
+    bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y)
+    rows = _rows_sample(M, n=24, seed=5)
+    ra, rsa = OQ.fp8_rowblock(a32[rows])
+    rb, rsb = OQ.fp8_tile(b32)
+    assert_bytes_equal(host(aq)[rows], ra, "a codes (sampled rows)")
+    assert_bytes_equal(host(bq), rb, "b codes")
+    yr, T = OM.blockwise_fp8(ra, rb, rsa, rsb)
+    assert_within_T(host(y)[rows], yr, T, "y rows")
+
+
+def test_blockwise_bf16_output_and_edges():
+    torch = _torch()
+    M, N, K = 130, 256, 384
+    say("blockwise bf16 out", M, N, K)
+    a, b, sa, sb = _recipe_blockwise(M, N, K, 800)
+    y = _run_blockwise(a, b, sa, sb, out_dtype=torch.bfloat16)
+    yr, T = OM.blockwise_fp8(a, b, sa, sb)
+    yb = OF.decode_bf16(host(y))
+    assert_within_T(yb, yr, T, "y bf16", bf16=True)
+    # M = 0 is a no-op; K = 0 gives zeros
+    say("blockwise M=0, K=0")
+    e = filled((0, N), torch.float32, 1.0)
+    bsq.bsq_blockwise_fp8_matmul(empty((0, K), torch.uint8), to_dev(b), empty((0, K // 128), torch.float32),
+                                 to_dev(sb), e)
+    z = filled((M, N), torch.float32, 1.0)
+    bsq.bsq_blockwise_fp8_matmul(empty((M, 0), torch.uint8), empty((N, 0), torch.uint8),
+                                 empty((M, 0), torch.float32), empty((N // 128, 0), torch.float32), z)
+    assert np.all(host(z) == 0.0)
+
+
+def test_blockwise_is_deterministic():
+    M, N, K = 1000, 2048, 2048
+    say("blockwise determinism", M, N, K)
+    a, b, sa, sb = _random_blockwise(M, N, K, 900)
+    y1 = host(_run_blockwise(a, b, sa, sb))
+    y2 = host(_run_blockwise(a, b, sa, sb))
+    assert_bytes_equal(y1.view(np.uint32), y2.view(np.uint32), "two runs")
+
+
+def test_blockwise_group_n_1_via_scaled_matmul_f32():
+    """scaled_matmul with float32 scales, block 128 on both operands (one
+    B scale per row)."""
+    torch = _torch()
+    Bt, M, N, K = 2, 70, 144, 512
+    say("scaled_matmul f32 scales", Bt, M, N, K)
+    a, sa = OQ.fp8_rowblock(synth.randn_f32((Bt * M, K), 41))
+    b, sb = OQ.fp8_rowblock(synth.randn_f32((Bt * N, K), 42))
+    a, sa = a.reshape(Bt, M, K), sa.reshape(Bt, M, K // 128)
+    b, sb = b.reshape(Bt, N, K), sb.reshape(Bt, N, K // 128)
+    y = filled((Bt, M, N), torch.float32, float("nan"))
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y,
+                          lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_F32)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, "e4m3", "e4m3", "f32")
+    assert_within_T(host(y), yr, T, "y")
+
+
+# ---------------------------------------------------------------- MX -------
+
+def _mx_scaled_abs(codes, scales, fmt):
+    return np.abs(OF.decode(codes, fmt)) * np.repeat(OF.decode_e8m0(scales), 32, axis=-1)
+
+
+@pytest.mark.parametrize("lf,rf,out", [("e4m3", "e4m3", "f32"), ("e5m2", "e4m3", "f32"),
+                                       ("e4m3", "e5m2", "bf16"), ("e5m2", "e5m2", "bf16")])
+def test_scaled_matmul_mx_small(lf, rf, out):
+    """Operands as the MXFP8 workload draws them: MX-quantized randn codes,
+    scale exponents uniform on -3..3."""
+    torch = _torch()
+    Bt, M, N, K = 3, 100, 272, 512
+    say("scaled_matmul mx", lf, rf, out)
+    a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 51), lf)
+    b, _ = OQ.mx(synth.randn_f32((Bt, N, K), 52), rf)
+    sa = synth.random_e8m0_codes((Bt, M, K // 32), 53)
+    sb = synth.random_e8m0_codes((Bt, N, K // 32), 54)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = filled((Bt, M, N), od, float("nan"))
+    code = {"e4m3": bsq.BSQ_E4M3, "e5m2": bsq.BSQ_E5M2}
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=code[lf],
+                          rhs_dtype=code[rf], scale_dtype=bsq.BSQ_E8M0)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, lf, rf, "e8m0")
+    yh = host(y) if out == "f32" else OF.decode_bf16(host(y))
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
+
+
+@pytest.mark.parametrize("lf,rf", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e5m2", "e5m2")])
+def test_scaled_matmul_mx_full_range_codes(lf, rf):
+    """Uniformly random codes and scale exponents over -8..8."""
+    torch = _torch()
+    Bt, M, N, K = 3, 100, 272, 512
+    say("scaled_matmul mx random codes", lf, rf)
+    a = synth.random_fp8_codes((Bt, M, K), 55, lf)
+    b = synth.random_fp8_codes((Bt, N, K), 56, rf)
+    sa = synth.random_e8m0_codes((Bt, M, K // 32), 57, -8, 8)
+    sb = synth.random_e8m0_codes((Bt, N, K // 32), 58, -8, 8)
+    y = filled((Bt, M, N), torch.float32, float("nan"))
+    code = {"e4m3": bsq.BSQ_E4M3, "e5m2": bsq.BSQ_E5M2}
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=code[lf],
+                          rhs_dtype=code[rf], scale_dtype=bsq.BSQ_E8M0)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, lf, rf, "e8m0")
+    G = fp8_group_bound(_mx_scaled_abs(a, sa, lf), _mx_scaled_abs(b, sb, rf))
+    assert_within_T_hw(host(y), yr, T, G, "y")
+
+
+def test_scaled_matmul_mx_batched_full_size_sampled():
+    """The MXFP8 batched workload: B=8, M=N=2048, K=4096, codes from the MX
+    quantizer of randn, scale exponents uniform on -3..3."""
+    torch = _torch()
+    Bt, M, N, K = 8, 2048, 2048, 4096
+    say("scaled_matmul mx full size", Bt, M, N, K)
+    lhs32 = synth.randn_f32((Bt * M, K), 30)
+    rhs32 = synth.randn_f32((Bt * N, K), 31)
+    lq = empty((Bt * M, K), torch.uint8)
+    rq = empty((Bt * N, K), torch.uint8)
+    junk_l = empty((Bt * M, K // 32), torch.uint8)
+    junk_r = empty((Bt * N, K // 32), torch.uint8)
+    bsq.bsq_quant_mx(to_dev(lhs32), lq, junk_l, axis=1, code_dtype=bsq.BSQ_E4M3)
+    bsq.bsq_quant_mx(to_dev(rhs32), rq, junk_r, axis=1, code_dtype=bsq.BSQ_E4M3)
+    sa = synth.random_e8m0_codes((Bt, M, K // 32), 32)
+    sb = synth.random_e8m0_codes((Bt, N, K // 32), 33)
+    y = filled((Bt, M, N), torch.float32, float("nan"))
+    bsq.bsq_scaled_matmul(lq.view(Bt, M, K), rq.view(Bt, N, K), to_dev(sa), to_dev(sb), y,
+                          lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_E8M0)
+    yh = host(y)
+    lqh = host(lq).reshape(Bt, M, K)
+    rqh = host(rq).reshape(Bt, N, K)
+    for bi in (0, 7):
+        rows = _rows_sample(M, n=12, seed=bi)
+        # the codes of these rows are the oracle's
+        rc, _ = OQ.mx(lhs32[bi * M + rows], "e4m3")
+        assert_bytes_equal(lqh[bi][rows], rc, f"lhs codes batch {bi}")
+        yr, T = OM.scaled_matmul(lqh[bi][rows][None], rqh[bi][None], sa[bi][rows][None], sb[bi][None],
+                                 "e4m3", "e4m3", "e8m0")
+        assert_within_T(yh[bi][rows], yr[0], T[0], f"y batch {bi}")
+    assert np.all(np.isfinite(yh))
+
+
+# ---------------------------------------------------------------- int8 -----
+
+@pytest.mark.parametrize("B,Din,Dout", [(2048, 4096, 4096), (7, 256, 48), (5, 63, 6), (300, 384, 272)])
+def test_int8_matmul(B, Din, Dout):
+    torch = _torch()
+    say("int8 matmul", B, Din, Dout)
+    x, w = synth.int8_workload(B, Din, Dout, 10, 11, zero_rows=(7, 1000), zero_cols=(3, 2047))
+    xq = empty((B, Din), torch.int8)
+    xs = empty((B,), torch.float32)
+    wq = empty((Din, Dout), torch.int8)
+    ws = empty((Dout,), torch.float32)
+    y = filled((B, Dout), torch.float32, float("nan"))
+    acc = empty((B, Dout), torch.int32)
+    work = empty((max(bsq.bsq_int8_workspace_bytes(Din, Dout), 16),), torch.uint8)
+    wqT = work[: Din * Dout].view(Dout, Din).view(torch.int8)
+    bsq.bsq_int8_quant_rows(to_dev(x), xq, xs)
+    bsq.bsq_int8_quant_cols(to_dev(w), wq, ws, wqT)
+    bsq.bsq_int8_matmul(xq, wqT, xs, ws, y, acc)
+    rxq, rxs = OQ.int8_rows(x)
+    rwq, rws = OQ.int8_cols(w)
+    a, y64, y32 = OM.int8_matmul(rxq, rwq, rxs, rws)
+    assert_bytes_equal(host(acc), a.astype(np.int32), "int32 sums")
+    yg = host(y)
+    assert_bytes_equal(yg.view(np.uint32), y32.view(np.uint32), "y")
+    assert np.all(np.abs(yg - y64) <= 1e-6 * np.abs(y64))
+    assert np.all(yg[a == 0] == 0.0)
+
+
+# ------------------------------------------------------------ backward -----
+
+def _lossless_bits(shape, seed):
+    g = synth.rng(seed)
+    mant = 1.0 + g.integers(0, 4, shape) / 4.0
+    e = g.integers(0, 4, shape)
+    sign = np.where(g.integers(0, 2, shape) == 1, -1.0, 1.0)
+    v = (sign * mant * np.exp2(e)).astype(np.float32)
+    return OF.encode_bf16(v), v.astype(np.float64)
+
+
+def _run_backward(dYb, Wb, Xb, out_dtype, code):
+    torch = _torch()
+    M, N = dYb.shape
+    K = Wb.shape[1]
+    dX = filled((M, K), out_dtype, float("nan"))
+    dW = filled((N, K), out_dtype, float("nan"))
+    ws = empty((bsq.bsq_mxfp8_backward_workspace_bytes(M, N, K),), torch.uint8)
+    bsq.bsq_mxfp8_backward(to_dev(dYb).view(torch.bfloat16), to_dev(Wb).view(torch.bfloat16),
+                           to_dev(Xb).view(torch.bfloat16), dX, dW, ws, code_dtype=code)
+    return dX, dW
+
+
+@pytest.mark.parametrize("fmt", ["e5m2", "e4m3"])
+def test_backward_lossless_inputs(fmt):
+    """Inputs whose MX quantization is lossless along both axes: dX and dW
+    equal the exact products of the inputs up to the float32 output
+    rounding."""
+    torch = _torch()
+    M, N, K = 384, 256, 512
+    say("backward lossless", fmt)
+    dYb, dY = _lossless_bits((M, N), 1)
+    Wb, W = _lossless_bits((N, K), 2)
+    Xb, X = _lossless_bits((M, K), 3)
+    code = bsq.BSQ_E5M2 if fmt == "e5m2" else bsq.BSQ_E4M3
+    dX, dW = _run_backward(dYb, Wb, Xb, torch.float32, code)
+    exact_dX, exact_dW = dY @ W, dY.T @ X
+    assert_within_T(host(dX), exact_dX, np.abs(dY) @ np.abs(W), "dX")
+    assert_within_T(host(dW), exact_dW, np.abs(dY).T @ np.abs(X), "dW")
+
+
+def test_backward_full_size_sampled():
+    """The MXFP8 backward workload: dY [8192, 4096], W [4096, 4096],
+    X [8192, 4096] bf16 randn, e5m2, bf16 outputs; sampled rows of dX and
+    dW against the oracle's scaled_matmul of its own quantized operands."""
+    torch = _torch()
+    M, N, K = 8192, 4096, 4096
+    say("backward full size", M, N, K)
+    dYb = synth.randn_bf16_bits((M, N), 40)
+    Wb = synth.randn_bf16_bits((N, K), 41)
+    Xb = synth.randn_bf16_bits((M, K), 42)
+    dX, dW = _run_backward(dYb, Wb, Xb, torch.bfloat16, bsq.BSQ_E5M2)
+    dXh = OF.decode_bf16(host(dX))
+    dWh = OF.decode_bf16(host(dW))
+    dY = OF.decode_bf16(dYb).astype(np.float32)
+    W = OF.decode_bf16(Wb).astype(np.float32)
+    X = OF.decode_bf16(Xb).astype(np.float32)
+    # dX rows r need dY rows r (blocked along N) and all of W (along N)
+    rows = _rows_sample(M, n=10, seed=1)
+    a, sa = OQ.mx_axis(dY[rows], 1, "e5m2")
+    b, sb = OQ.mx_axis(W, 0, "e5m2")
+    yr, T = OM.scaled_matmul(a[None], b[None], sa[None], sb[None], "e5m2", "e5m2", "e8m0")
+    assert_within_T(dXh[rows], yr[0], T[0], "dX rows", bf16=True)
+    # dW rows n need column n of dY (blocked along M) and all of X (along M)
+    nrows = _rows_sample(N, n=10, seed=2)
+    a, sa = OQ.mx_axis(np.ascontiguousarray(dY[:, nrows]), 0, "e5m2")
+    b, sb = OQ.mx_axis(X, 0, "e5m2")
+    yr, T = OM.scaled_matmul(a[None], b[None], sa[None], sb[None], "e5m2", "e5m2", "e8m0")
+    assert_within_T(dWh[nrows], yr[0], T[0], "dW rows", bf16=True)
+    assert np.all(np.isfinite(dXh)) and np.all(np.isfinite(dWh))
