@@ -142,6 +142,15 @@ def run_main(args):
     except (OSError, ValueError):
         traffic = None
 
+    if args.calibrate_copy:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        nbytes = 512 << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        _log(f"[bench] calibration copy: 5 x {nbytes} bytes read and written")
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": METRIC,
@@ -343,6 +352,8 @@ def main():
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "suite.jsonl"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy 512 MiB five times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this library's path runs on a single MI355X and has no "

@@ -37,6 +37,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int THREADS = 512;
@@ -61,13 +62,38 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int off0, int off1)
   return r;
 }
 
+// Buffer resource (V#) of a raw byte buffer: base, no stride, `records`
+// bytes in range (clamped to [0, 2^31)); offsets at or past the end read as
+// zero.  dword3 0x00020000 = 32-bit data format, the gfx9 raw-buffer value.
+__device__ __forceinline__ i32x4 raw_rsrc(const uint8_t* base, int64_t records) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const int n = int(records < 0 ? 0 : (records > 0x7FFFFFFF ? 0x7FFFFFFF : records));
+  return i32x4{int(uint32_t(b)), int(uint32_t(b >> 32) & 0xFFFFu), n, 0x00020000};
+}
+
+// 16 bytes per lane from buffer `rsrc` at byte offset `voff` straight into
+// LDS: lane i writes [lds_addr + 16 i, lds_addr + 16 i + 16).  Issued as
+// inline asm so that the compiler does not order it against the fragment
+// reads of the other LDS stage; the caller waits with vmcnt(0) before the
+// barrier that publishes the stage.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
+}
+
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
 __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
-  __shared__ uint32_t lds_sa[2][BM];
-  __shared__ uint32_t lds_sb[2][BN];
-  __shared__ uint32_t lds_dummy[64];
+  // per-step scales: [0, 256) one word per A row, [256, 512) one per B row
+  // (MX, FP8G with GN1) or per 128-row B group (FP8G)
+  __shared__ uint32_t lds_s[2][THREADS];
 
   const int tid = threadIdx.x;
   const int batch = blockIdx.z;
@@ -79,65 +105,49 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
   const uint8_t* A = p.A + int64_t(batch) * p.sA;
   const uint8_t* B = p.B + int64_t(batch) * p.sB;
 
-  // ---- global -> LDS: direct 16-byte loads (global_load_lds_dwordx4).
-  // Lane i of a wave fills LDS bytes [16 i, 16 i + 16) of the wave's 1 KiB
-  // slice, i.e. row (wave_row0 + i / 8), physical chunk i % 8; it fetches
-  // the logical chunk that the XOR swizzle stores there.  Each wave moves
-  // 4 slices of A and 4 of B per K-step (rows 8w + 64 s .. + 8).
+  // ---- global -> LDS: direct 16-byte buffer loads.  Lane i of a wave
+  // fills LDS bytes [16 i, 16 i + 16) of the wave's 1 KiB slice, i.e. row
+  // (wave_row0 + i / 8), physical chunk i % 8; it fetches the logical chunk
+  // that the XOR swizzle stores there.  Each wave moves 4 slices of A and 4
+  // of B per K-step (rows 8w + 64 s .. + 8).  One descriptor per slice
+  // (scalar registers) starts at that slice's first row and K-step; rows at
+  // or past M (N) fall outside its range and read as zero, so tails need no
+  // clamping.
   const int w = tid >> 6, lane = tid & 63;
-  const int lrow = 8 * w + (lane >> 3);  // + 64 s
-  const int lphys = lane & 7;
-  const int llog = lphys ^ (lrow & 7);
-  const uint8_t* gA[4];
-  const uint8_t* gB[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int r = lrow + 64 * s;
-    gA[s] = A + int64_t(min(m0 + r, M - 1)) * K + 16 * llog;
-    gB[s] = B + int64_t(min(n0 + r, N - 1)) * K + 16 * llog;
-  }
+  const int lrow = 8 * w + (lane >> 3);
+  const int llog = (lane & 7) ^ (lrow & 7);
+  const int voff = lrow * K + 16 * llog;  // < 64 K
+  const int64_t a_bytes = int64_t(M) * K, b_bytes = int64_t(N) * K;
+  const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&lds_a[0][8 * w * BK]));
+  const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&lds_b[0][8 * w * BK]));
   auto gload = [&](int ks, int st) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int slice = (8 * w + 64 * s) * BK;  // wave-uniform LDS byte offset
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(gA[s] + int64_t(ks) * BK),
-          (__attribute__((address_space(3))) void*)(&lds_a[st][slice]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(gB[s] + int64_t(ks) * BK),
-          (__attribute__((address_space(3))) void*)(&lds_b[st][slice]), 16, 0, 0);
+      const int64_t oa = int64_t(m0 + 64 * s) * K + int64_t(ks) * BK;
+      const int64_t ob = int64_t(n0 + 64 * s) * K + int64_t(ks) * BK;
+      const uint32_t soff = uint32_t(st * BM * BK + 64 * s * BK);
+      lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + soff);
+      lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + soff);
     }
   };
 
-  // ---- per-step scales, staged through one register into LDS.
-  // FP8G: thread t < 256 loads the A scale of row t; B scales per row (GN1)
-  // or per 128-row group.  MX: 4 E8M0 bytes per row per step.  Threads
-  // without a scale to move read a valid word and write a dummy LDS slot,
-  // so the loop body has no divergent branches.
+  // ---- per-step scales, one word per thread through a register.  Threads
+  // without a scale to move read a valid word (row 0 of the A scales) into
+  // a slot nobody reads, so the loop body has no divergent branch.
+  constexpr bool kScales = MODE != MODE_I8;
   const uint32_t* sptr = nullptr;
-  uint32_t* sdst[2] = {&lds_dummy[tid & 63], &lds_dummy[tid & 63]};
   if (MODE == MODE_FP8G) {
     const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + int64_t(batch) * p.sSA;
     const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + int64_t(batch) * p.sSB;
     sptr = SA;
-    if (tid < 256) {
-      sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
-    } else if (GN1) {
-      sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
-    } else if (tid - 256 < 2 && n0 + 128 * (tid - 256) < N) {
-      sptr = SB + int64_t(n0 / 128 + (tid - 256)) * nk;
-    }
-    if (tid < 256 || GN1 || (tid - 256 < 2 && n0 + 128 * (tid - 256) < N)) {
-      sdst[0] = tid < 256 ? &lds_sa[0][tid] : &lds_sb[0][tid - 256];
-      sdst[1] = tid < 256 ? &lds_sa[1][tid] : &lds_sb[1][tid - 256];
-    }
+    if (tid < 256) sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
+    else if (GN1) sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
+    else if (tid - 256 < 2 && n0 + 128 * (tid - 256) < N) sptr = SB + int64_t(n0 / 128 + (tid - 256)) * nk;
   } else if (MODE == MODE_MX) {
     const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + p.sSA / 4 * batch;
     const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + p.sSB / 4 * batch;
     if (tid < 256) sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
     else sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
-    sdst[0] = tid < 256 ? &lds_sa[0][tid] : &lds_sb[0][tid - 256];
-    sdst[1] = tid < 256 ? &lds_sa[1][tid] : &lds_sb[1][tid - 256];
   }
 
   // ---- wave / lane roles in the MFMA loop
@@ -153,23 +163,23 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
 
-  constexpr bool kScales = MODE != MODE_I8;
   gload(0, 0);
-  if (kScales) *sdst[0] = sptr[0];
+  if (kScales) lds_s[0][tid] = sptr[0];
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
   __syncthreads();
 
+  // The next step's tiles stream into the idle stage while this one is
+  // multiplied.  The final step reloads its own tile into the idle stage so
+  // that the body has no branch.
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks & 1;
-    // the next step's tiles and scales; the last step reloads its own tile
-    // into the idle buffer so that the body has no branch
     const int kn = min(ks + 1, nk - 1);
     gload(kn, st ^ 1);
-    uint32_t s_next = 0;
-    if (kScales) s_next = sptr[kn];
+    const uint32_t s_next = kScales ? sptr[kn] : 0u;
 
     const uint8_t* ta = lds_a[st];
     const uint8_t* tb = lds_b[st];
+    const uint32_t* ss = lds_s[st];
     v8i q[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -181,11 +191,11 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
     float sbg = 0.f;
     if (MODE == MODE_FP8G) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = __uint_as_float(lds_sa[st][64 * wm + 16 * i + r16]);
-      if (!GN1) sbg = __uint_as_float(lds_sb[st][wn]);
+      for (int i = 0; i < 4; ++i) sa[i] = __uint_as_float(ss[64 * wm + 16 * i + r16]);
+      if (!GN1) sbg = __uint_as_float(ss[256 + wn]);
     } else if (MODE == MODE_MX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qa[i] = int((lds_sa[st][64 * wm + 16 * i + r16] >> (8 * g)) & 0xFFu);
+      for (int i = 0; i < 4; ++i) qa[i] = int((ss[64 * wm + 16 * i + r16] >> (8 * g)) & 0xFFu);
     }
     v8i pb = lds_frag(tb, (128 * wn + r16) * BK + c0, (128 * wn + r16) * BK + c1);
 #pragma unroll
@@ -196,7 +206,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
       if (MODE == MODE_FP8G) {
         float sb4[4];
         if (GN1) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&lds_sb[st][128 * wn + 16 * j + 4 * g]);
+          const uint4 v = *reinterpret_cast<const uint4*>(&ss[256 + 128 * wn + 16 * j + 4 * g]);
           sb4[0] = __uint_as_float(v.x); sb4[1] = __uint_as_float(v.y);
           sb4[2] = __uint_as_float(v.z); sb4[3] = __uint_as_float(v.w);
         }
@@ -214,7 +224,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
           }
         }
       } else if (MODE == MODE_MX) {
-        const int qb = int((lds_sb[st][rowb] >> (8 * g)) & 0xFFu);
+        const int qb = int((ss[256 + rowb] >> (8 * g)) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], acc[j][i], FB, FA, 0,
@@ -234,7 +244,7 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (kScales) *sdst[st ^ 1] = s_next;
+    if (kScales) lds_s[st ^ 1][tid] = s_next;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
