@@ -97,8 +97,28 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int batch = blockIdx.z;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear
+  // id and each XCD has its own L2, so the tiles one XCD receives should
+  // share operand rows: linear id L goes to XCD L % 8 as its (L / 8)-th
+  // workgroup; XCD x gets the x-th contiguous eighth of a tile order that
+  // walks column-major through bands of kBand tile rows, i.e. a compact
+  // block of tiles (4 x 8 for a 16 x 16 grid).
+  int tm, tn;
+  {
+    constexpr int kBand = 4;
+    const int tiles_n = gridDim.x, tiles_m = gridDim.y;
+    const int T = tiles_n * tiles_m;
+    const int L = blockIdx.y * tiles_n + blockIdx.x;
+    const int per = T / 8;
+    const int t = (L < 8 * per) ? (L % 8) * per + L / 8 : L;
+    const int band = t / (kBand * tiles_n);
+    const int rows = min(kBand, tiles_m - band * kBand);
+    const int in = t - band * kBand * tiles_n;
+    tm = band * kBand + in % rows;
+    tn = in / rows;
+  }
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int nk = K / BK;
 
@@ -180,14 +200,25 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
     const uint8_t* ta = lds_a[st];
     const uint8_t* tb = lds_b[st];
     const uint32_t* ss = lds_s[st];
+    // Fragment reads are issued in the order their MFMAs need them (the
+    // first MFMA waits only for its own two fragments); all of the step's
+    // scales are read before the loop, because a scale read between the
+    // fragment reads would make its wait drain the fragment prefetches too
+    // (LDS reads retire in order).  B fragments stream two ahead.
+    auto afrag = [&](int i) {
+      const int row = 64 * wm + 16 * i + r16;
+      return lds_frag(ta, row * BK + c0, row * BK + c1);
+    };
+    auto bfrag = [&](int j) {
+      const int rowb = 128 * wn + 16 * j + r16;
+      return lds_frag(tb, rowb * BK + c0, rowb * BK + c1);
+    };
+    v8i p0 = bfrag(0);
     v8i q[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 64 * wm + 16 * i + r16;
-      q[i] = lds_frag(ta, row * BK + c0, row * BK + c1);
-    }
+    for (int i = 0; i < 4; ++i) q[i] = afrag(i);
     float sa[4];
-    int qa[4];
+    int qa[4], qb[8];
     float sbg = 0.f;
     if (MODE == MODE_FP8G) {
 #pragma unroll
@@ -196,39 +227,55 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
     } else if (MODE == MODE_MX) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) qa[i] = int((ss[64 * wm + 16 * i + r16] >> (8 * g)) & 0xFFu);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qb[j] = int((ss[256 + 128 * wn + 16 * j + r16] >> (8 * g)) & 0xFFu);
     }
-    v8i pb = lds_frag(tb, (128 * wn + r16) * BK + c0, (128 * wn + r16) * BK + c1);
+    v8i p1 = bfrag(1);
+    // FP8G: the rescale of block j-1 runs on the VALU between the MFMAs of
+    // block j, which do not depend on it.
+    v4f dprev[4];
+    float sb4p[4];
+    auto rescale = [&](int jj, const v4f (&d)[4], const float (&sb4)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (GN1) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[jj][i][r] = fmaf(d[i][r], sa[i] * sb4[r], acc[jj][i][r]);
+        } else {
+          const float sc = sa[i] * sbg;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[jj][i][r] = fmaf(d[i][r], sc, acc[jj][i][r]);
+        }
+      }
+    };
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int rowb = 128 * wn + 16 * j + r16;
-      v8i pn;
-      if (j < 7) pn = lds_frag(tb, (rowb + 16) * BK + c0, (rowb + 16) * BK + c1);
+      v8i p2;
+      if (j + 2 < 8) p2 = bfrag(j + 2);
+      const v8i pb = p0;
       if (MODE == MODE_FP8G) {
-        float sb4[4];
+        float sb4[4] = {0.f, 0.f, 0.f, 0.f};
         if (GN1) {
           const uint4 v = *reinterpret_cast<const uint4*>(&ss[256 + 128 * wn + 16 * j + 4 * g]);
           sb4[0] = __uint_as_float(v.x); sb4[1] = __uint_as_float(v.y);
           sb4[2] = __uint_as_float(v.z); sb4[3] = __uint_as_float(v.w);
         }
+        v4f dcur[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
-          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], zero, 0, 0, 0, 0, 0, 0);
-          if (GN1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(d[r], sa[i] * sb4[r], acc[j][i][r]);
-          } else {
-            const float sc = sa[i] * sbg;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(d[r], sc, acc[j][i][r]);
-          }
+          dcur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], zero, 0, 0, 0, 0, 0, 0);
         }
+        if (j > 0) rescale(j - 1, dprev, sb4p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dprev[i] = dcur[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sb4p[r] = sb4[r];
       } else if (MODE == MODE_MX) {
-        const int qb = int((ss[256 + rowb] >> (8 * g)) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], acc[j][i], FB, FA, 0,
-                                                                       qb, 0, qa[i]);
+                                                                       qb[j], 0, qa[i]);
       } else {
         const v4i plo = {pb[0], pb[1], pb[2], pb[3]};
         const v4i phi = {pb[4], pb[5], pb[6], pb[7]};
@@ -240,9 +287,21 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
           acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(phi, qhi, acc[j][i], 0, 0, 0);
         }
       }
-      if (j < 7) pb = pn;
+      p0 = p1;
+      if (j + 2 < 8) p1 = p2;
+      if (MODE == MODE_FP8G && j > 0) {
+        // issue order: the two prefetch reads, then one MFMA followed by
+        // four rescale FMAs, four times
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (MODE == MODE_FP8G) rescale(7, dprev, sb4p);
 
     if (kScales) lds_s[st ^ 1][tid] = s_next;
     __builtin_amdgcn_s_waitcnt(0x0F70);
