@@ -40,7 +40,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int THREADS = 512;
 
 struct GemmArgs {
   const uint8_t* A;
@@ -87,13 +86,26 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
-__global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
+// NW waves per workgroup.  NW = 8: waves 4 (M) x 2 (N), each 64 x 128 (4 x 8
+// blocks), accumulators in VGPRs - the FP8G rescale needs them on the VALU.
+// NW = 4: waves 2 x 2, each 128 x 128 (8 x 8 blocks); the MX and I8
+// accumulators never leave the matrix core's reach (AGPRs), and the larger
+// wave tile reads 1.5x fewer fragment bytes from LDS per MFMA.
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
+  static_assert(NW == 8 || NW == 4, "4 or 8 waves");
+  static_assert(MODE != MODE_FP8G || NW == 8, "the FP8G rescale keeps its accumulators in VGPRs");
+  constexpr int NT = 64 * NW;          // threads
+  constexpr int WGM = NW == 8 ? 4 : 2;  // waves along M
+  constexpr int MB = BM / WGM / 16;     // 16-row blocks per wave along M
+  constexpr int NB = 8;                 // 16-column blocks per wave along N
+  constexpr int SPW = 32 / NW;          // 8-row DMA slices per wave per operand
+
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
   // per-step scales: [0, 256) one word per A row, [256, 512) one per B row
   // (MX, FP8G with GN1) or per 128-row B group (FP8G)
-  __shared__ uint32_t lds_s[2][THREADS];
+  __shared__ uint32_t lds_s[2][512];
 
   const int tid = threadIdx.x;
   const int batch = blockIdx.z;
@@ -126,65 +138,77 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
   const uint8_t* B = p.B + int64_t(batch) * p.sB;
 
   // ---- global -> LDS: direct 16-byte buffer loads.  Lane i of a wave
-  // fills LDS bytes [16 i, 16 i + 16) of the wave's 1 KiB slice, i.e. row
-  // (wave_row0 + i / 8), physical chunk i % 8; it fetches the logical chunk
-  // that the XOR swizzle stores there.  Each wave moves 4 slices of A and 4
-  // of B per K-step (rows 8w + 64 s .. + 8).  One descriptor per slice
-  // (scalar registers) starts at that slice's first row and K-step; rows at
-  // or past M (N) fall outside its range and read as zero, so tails need no
-  // clamping.
-  const int w = tid >> 6, lane = tid & 63;
+  // fills LDS bytes [16 i, 16 i + 16) of one 1 KiB slice (8 rows x 128
+  // bytes), i.e. row (slice_row0 + i / 8), physical chunk i % 8; it fetches
+  // the logical chunk that the XOR swizzle stores there.  Wave w moves
+  // slices w, w + NW, ... of A and of B per K-step.  One descriptor per
+  // slice (scalar registers) starts at that slice's first row and K-step;
+  // rows at or past M (N) fall outside its range and read as zero, so
+  // tails need no clamping.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = 8 * w + (lane >> 3);
   const int llog = (lane & 7) ^ (lrow & 7);
-  const int voff = lrow * K + 16 * llog;  // < 64 K
+  const int voff = lrow * K + 16 * llog;  // < 8 NW K
   const int64_t a_bytes = int64_t(M) * K, b_bytes = int64_t(N) * K;
   const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&lds_a[0][8 * w * BK]));
   const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&lds_b[0][8 * w * BK]));
   auto gload = [&](int ks, int st) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t oa = int64_t(m0 + 64 * s) * K + int64_t(ks) * BK;
-      const int64_t ob = int64_t(n0 + 64 * s) * K + int64_t(ks) * BK;
-      const uint32_t soff = uint32_t(st * BM * BK + 64 * s * BK);
+    for (int s = 0; s < SPW; ++s) {
+      const int64_t oa = int64_t(m0 + 8 * NW * s) * K + int64_t(ks) * BK;
+      const int64_t ob = int64_t(n0 + 8 * NW * s) * K + int64_t(ks) * BK;
+      const uint32_t soff = uint32_t(st * BM * BK + 8 * NW * s * BK);
       lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + soff);
       lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + soff);
     }
   };
 
-  // ---- per-step scales, one word per thread through a register.  Threads
-  // without a scale to move read a valid word (row 0 of the A scales) into
-  // a slot nobody reads, so the loop body has no divergent branch.
+  // ---- per-step scales, one word per slot through a register: slot
+  // r < 256 is A row r, slot 256 + r is B row (or group) r.  Each thread
+  // moves slots tid, tid + NT, ...  Slots with nothing to move read a valid
+  // word (row 0 of the A scales) into a place nobody reads, so the loop
+  // body has no divergent branch.
   constexpr bool kScales = MODE != MODE_I8;
-  const uint32_t* sptr = nullptr;
-  if (MODE == MODE_FP8G) {
-    const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + int64_t(batch) * p.sSA;
-    const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + int64_t(batch) * p.sSB;
-    sptr = SA;
-    if (tid < 256) sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
-    else if (GN1) sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
-    else if (tid - 256 < 2 && n0 + 128 * (tid - 256) < N) sptr = SB + int64_t(n0 / 128 + (tid - 256)) * nk;
-  } else if (MODE == MODE_MX) {
-    const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + p.sSA / 4 * batch;
-    const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + p.sSB / 4 * batch;
-    if (tid < 256) sptr = SA + int64_t(min(m0 + tid, M - 1)) * nk;
-    else sptr = SB + int64_t(min(n0 + tid - 256, N - 1)) * nk;
+  constexpr int SPT = 512 / NT;  // scale slots per thread
+  const uint32_t* sptr[SPT];
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int slot = tid + NT * u;
+    sptr[u] = nullptr;
+    if (MODE == MODE_FP8G) {
+      const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + int64_t(batch) * p.sSA;
+      const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + int64_t(batch) * p.sSB;
+      const int r = slot - 256;
+      sptr[u] = SA;
+      if (slot < 256) sptr[u] = SA + int64_t(min(m0 + slot, M - 1)) * nk;
+      else if (GN1) sptr[u] = SB + int64_t(min(n0 + r, N - 1)) * nk;
+      else if (r < 2 && n0 + 128 * r < N) sptr[u] = SB + int64_t(n0 / 128 + r) * nk;
+    } else if (MODE == MODE_MX) {
+      const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + p.sSA / 4 * batch;
+      const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + p.sSB / 4 * batch;
+      if (slot < 256) sptr[u] = SA + int64_t(min(m0 + slot, M - 1)) * nk;
+      else sptr[u] = SB + int64_t(min(n0 + slot - 256, N - 1)) * nk;
+    }
   }
 
   // ---- wave / lane roles in the MFMA loop
-  const int wm = w & 3, wn = w >> 2;
+  const int wm = w % WGM, wn = w / WGM;
   const int g = lane >> 4, r16 = lane & 15;
   const int swz = r16 & 7;
   const int c0 = 16 * (g ^ swz), c1 = 16 * ((g + 4) ^ swz);
 
   typedef typename std::conditional<MODE == MODE_I8, v4i, v4f>::type acc_t;
-  acc_t acc[8][4];
+  acc_t acc[NB][MB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
+    for (int i = 0; i < MB; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
 
   gload(0, 0);
-  if (kScales) lds_s[0][tid] = sptr[0];
+  if (kScales) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) lds_s[0][tid + NT * u] = sptr[u][0];
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
   __syncthreads();
 
@@ -195,49 +219,52 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
     const int st = ks & 1;
     const int kn = min(ks + 1, nk - 1);
     gload(kn, st ^ 1);
-    const uint32_t s_next = kScales ? sptr[kn] : 0u;
+    uint32_t s_next[SPT];
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) s_next[u] = kScales ? sptr[u][kn] : 0u;
 
     const uint8_t* ta = lds_a[st];
     const uint8_t* tb = lds_b[st];
     const uint32_t* ss = lds_s[st];
-    // Fragment reads are issued in the order their MFMAs need them (the
-    // first MFMA waits only for its own two fragments); all of the step's
-    // scales are read before the loop, because a scale read between the
-    // fragment reads would make its wait drain the fragment prefetches too
-    // (LDS reads retire in order).  B fragments stream two ahead.
+    // LDS reads retire in order, so a wait for one read also waits for all
+    // reads issued before it.  The step's scales are therefore read first,
+    // then the fragments in the order their MFMAs need them (the first MFMA
+    // waits only for the scales and its own two fragments); B fragments
+    // stream two ahead.
     auto afrag = [&](int i) {
-      const int row = 64 * wm + 16 * i + r16;
+      const int row = 16 * MB * wm + 16 * i + r16;
       return lds_frag(ta, row * BK + c0, row * BK + c1);
     };
     auto bfrag = [&](int j) {
       const int rowb = 128 * wn + 16 * j + r16;
       return lds_frag(tb, rowb * BK + c0, rowb * BK + c1);
     };
-    v8i p0 = bfrag(0);
-    v8i q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = afrag(i);
-    float sa[4];
-    int qa[4], qb[8];
+    float sa[MB];
+    uint32_t qa_w[MB], qb_w[NB];
     float sbg = 0.f;
     if (MODE == MODE_FP8G) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = __uint_as_float(ss[64 * wm + 16 * i + r16]);
+      for (int i = 0; i < MB; ++i) sa[i] = __uint_as_float(ss[16 * MB * wm + 16 * i + r16]);
       if (!GN1) sbg = __uint_as_float(ss[256 + wn]);
     } else if (MODE == MODE_MX) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qa[i] = int((ss[64 * wm + 16 * i + r16] >> (8 * g)) & 0xFFu);
+      for (int i = 0; i < MB; ++i) qa_w[i] = ss[16 * MB * wm + 16 * i + r16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) qb[j] = int((ss[256 + 128 * wn + 16 * j + r16] >> (8 * g)) & 0xFFu);
+      for (int j = 0; j < NB; ++j) qb_w[j] = ss[256 + 128 * wn + 16 * j + r16];
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the scale reads ahead of the fragment reads
+    v8i p0 = bfrag(0);
+    v8i q[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) q[i] = afrag(i);
     v8i p1 = bfrag(1);
     // FP8G: the rescale of block j-1 runs on the VALU between the MFMAs of
     // block j, which do not depend on it.
-    v4f dprev[4];
+    v4f dprev[MB];
     float sb4p[4];
-    auto rescale = [&](int jj, const v4f (&d)[4], const float (&sb4)[4]) {
+    auto rescale = [&](int jj, const v4f (&d)[MB], const float (&sb4)[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MB; ++i) {
         if (GN1) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[jj][i][r] = fmaf(d[i][r], sa[i] * sb4[r], acc[jj][i][r]);
@@ -249,9 +276,9 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
       }
     };
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       v8i p2;
-      if (j + 2 < 8) p2 = bfrag(j + 2);
+      if (j + 2 < NB) p2 = bfrag(j + 2);
       const v8i pb = p0;
       if (MODE == MODE_FP8G) {
         float sb4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -260,27 +287,30 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
           sb4[0] = __uint_as_float(v.x); sb4[1] = __uint_as_float(v.y);
           sb4[2] = __uint_as_float(v.z); sb4[3] = __uint_as_float(v.w);
         }
-        v4f dcur[4];
+        v4f dcur[MB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MB; ++i) {
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
           dcur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], zero, 0, 0, 0, 0, 0, 0);
         }
         if (j > 0) rescale(j - 1, dprev, sb4p);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dprev[i] = dcur[i];
+        for (int i = 0; i < MB; ++i) dprev[i] = dcur[i];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sb4p[r] = sb4[r];
       } else if (MODE == MODE_MX) {
+        // E8M0 scale bytes: byte g of the row's word covers this lane's
+        // 32-element K block (the instruction reads its scale from byte 0)
+        const int qb = int((qb_w[j] >> (8 * g)) & 0xFFu);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], acc[j][i], FB, FA, 0,
-                                                                       qb[j], 0, qa[i]);
+        for (int i = 0; i < MB; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              pb, q[i], acc[j][i], FB, FA, 0, qb, 0, int((qa_w[i] >> (8 * g)) & 0xFFu));
       } else {
         const v4i plo = {pb[0], pb[1], pb[2], pb[3]};
         const v4i phi = {pb[4], pb[5], pb[6], pb[7]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MB; ++i) {
           const v4i qlo = {q[i][0], q[i][1], q[i][2], q[i][3]};
           const v4i qhi = {q[i][4], q[i][5], q[i][6], q[i][7]};
           acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(plo, qlo, acc[j][i], 0, 0, 0);
@@ -288,35 +318,38 @@ __global__ void __launch_bounds__(THREADS, 1) k_gemm(GemmArgs p) {
         }
       }
       p0 = p1;
-      if (j + 2 < 8) p1 = p2;
+      if (j + 2 < NB) p1 = p2;
       if (MODE == MODE_FP8G && j > 0) {
         // issue order: the two prefetch reads, then one MFMA followed by
-        // four rescale FMAs, four times
+        // four rescale FMAs, MB times
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MB; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (MODE == MODE_FP8G) rescale(7, dprev, sb4p);
+    if (MODE == MODE_FP8G) rescale(NB - 1, dprev, sb4p);
 
-    if (kScales) lds_s[st ^ 1][tid] = s_next;
+    if (kScales) {
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) lds_s[st ^ 1][tid + NT * u] = s_next[u];
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
   // ---- epilogue
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 64 * wm + 16 * i + r16;
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + 16 * MB * wm + 16 * i + r16;
     if (m >= M) continue;
     float xs = 0.f;
     if (MODE == MODE_I8) xs = static_cast<const float*>(p.SA)[int64_t(batch) * p.sSA + m];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int n = n0 + 128 * wn + 16 * j + 4 * g;
       if (n >= N) continue;
       const int64_t o = int64_t(batch) * p.sC + int64_t(m) * N + n;
@@ -361,8 +394,9 @@ bsq_status zero_fill(void* p, int64_t bytes, hipStream_t st) {
 
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
 bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
+  constexpr int NW = 8;
   dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
-  hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1>), grid, THREADS, 0, st, a);
+  hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW>), grid, 64 * NW, 0, st, a);
   return launch_status("gemm");
 }
 
