@@ -82,6 +82,14 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, int voff, uint32_t lds_add
                : "memory", "m0");
 }
 
+// 4 bytes per lane: lane i writes [lds_addr + 4 i, lds_addr + 4 i + 4).
+__device__ __forceinline__ void lds_dma4(i32x4 rsrc, int voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
@@ -163,33 +171,43 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     }
   };
 
-  // ---- per-step scales, one word per slot through a register: slot
-  // r < 256 is A row r, slot 256 + r is B row (or group) r.  Each thread
-  // moves slots tid, tid + NT, ...  Slots with nothing to move read a valid
-  // word (row 0 of the A scales) into a place nobody reads, so the loop
-  // body has no divergent branch.
+  // ---- per-step scales, by direct 4-byte buffer loads into LDS as well:
+  // slot r < 256 holds the step's word of A row r, slot 256 + r that of B
+  // row r (MX, FP8G with GN1) or of B row group r (FP8G).  Lane i of wave w
+  // fills slot 64 w + i (NW = 8: waves 0-3 the A rows, 4-7 the B rows).
+  // Lanes with nothing to move read row 0 of their operand's scales into a
+  // slot nobody reads.
   constexpr bool kScales = MODE != MODE_I8;
-  constexpr int SPT = 512 / NT;  // scale slots per thread
-  const uint32_t* sptr[SPT];
-#pragma unroll
-  for (int u = 0; u < SPT; ++u) {
-    const int slot = tid + NT * u;
-    sptr[u] = nullptr;
+  static_assert(!kScales || NW == 8, "scale staging assumes 512 threads");
+  const uint8_t* sbase = nullptr;  // this wave's scale array at K-step 0
+  int soff_v = 0;                  // this lane's byte offset in it
+  int64_t s_records = 0;
+  if (kScales) {
+    // waves 0-3 (uniform w < 4) own the A slots, waves 4-7 the B slots
+    const bool a_side = w < 4;
+    const int r = tid - 256;
     if (MODE == MODE_FP8G) {
-      const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + int64_t(batch) * p.sSA;
-      const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + int64_t(batch) * p.sSB;
-      const int r = slot - 256;
-      sptr[u] = SA;
-      if (slot < 256) sptr[u] = SA + int64_t(min(m0 + slot, M - 1)) * nk;
-      else if (GN1) sptr[u] = SB + int64_t(min(n0 + r, N - 1)) * nk;
-      else if (r < 2 && n0 + 128 * r < N) sptr[u] = SB + int64_t(n0 / 128 + r) * nk;
-    } else if (MODE == MODE_MX) {
-      const uint32_t* SA = static_cast<const uint32_t*>(p.SA) + p.sSA / 4 * batch;
-      const uint32_t* SB = static_cast<const uint32_t*>(p.SB) + p.sSB / 4 * batch;
-      if (slot < 256) sptr[u] = SA + int64_t(min(m0 + slot, M - 1)) * nk;
-      else sptr[u] = SB + int64_t(min(n0 + slot - 256, N - 1)) * nk;
+      const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + int64_t(batch) * p.sSA * 4;
+      const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + int64_t(batch) * p.sSB * 4;
+      const int rows_b = GN1 ? N : N / 128;
+      sbase = a_side ? SA : SB;
+      s_records = (a_side ? int64_t(M) : int64_t(rows_b)) * nk * 4;
+      const int rb = GN1 ? min(n0 + r, N - 1) : ((r >= 0 && r < 2 && n0 + 128 * r < N) ? n0 / 128 + r : 0);
+      soff_v = (a_side ? min(m0 + tid, M - 1) : rb) * nk * 4;
+    } else {
+      const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + p.sSA * batch;
+      const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + p.sSB * batch;
+      sbase = a_side ? SA : SB;
+      s_records = (a_side ? int64_t(M) : int64_t(N)) * nk * 4;
+      soff_v = (a_side ? min(m0 + tid, M - 1) : min(n0 + r, N - 1)) * nk * 4;
     }
   }
+  const uint32_t ls_base = __builtin_amdgcn_readfirstlane(lds_addr_of(reinterpret_cast<const uint8_t*>(&lds_s[0][64 * w])));
+  auto sload = [&](int ks, int st) {
+    if (kScales)
+      lds_dma4(raw_rsrc(sbase + 4 * int64_t(ks), s_records - 4 * int64_t(ks)), soff_v,
+               ls_base + uint32_t(st * 512 * 4));
+  };
 
   // ---- wave / lane roles in the MFMA loop
   const int wm = w % WGM, wn = w / WGM;
@@ -205,10 +223,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     for (int i = 0; i < MB; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
 
   gload(0, 0);
-  if (kScales) {
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) lds_s[0][tid + NT * u] = sptr[u][0];
-  }
+  sload(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
   __syncthreads();
 
@@ -219,9 +234,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     const int st = ks & 1;
     const int kn = min(ks + 1, nk - 1);
     gload(kn, st ^ 1);
-    uint32_t s_next[SPT];
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) s_next[u] = kScales ? sptr[u][kn] : 0u;
+    sload(kn, st ^ 1);
 
     const uint8_t* ta = lds_a[st];
     const uint8_t* tb = lds_b[st];
@@ -230,7 +243,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     // reads issued before it.  The step's scales are therefore read first,
     // then the fragments in the order their MFMAs need them (the first MFMA
     // waits only for the scales and its own two fragments); B fragments
-    // stream two ahead.
+    // stream PF ahead.
     auto afrag = [&](int i) {
       const int row = 16 * MB * wm + 16 * i + r16;
       return lds_frag(ta, row * BK + c0, row * BK + c1);
@@ -253,11 +266,14 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       for (int j = 0; j < NB; ++j) qb_w[j] = ss[256 + 128 * wn + 16 * j + r16];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the scale reads ahead of the fragment reads
-    v8i p0 = bfrag(0);
+    constexpr int PF = 2;  // B fragments in flight ahead of their MFMAs
+    v8i pq[PF];
+    pq[0] = bfrag(0);
     v8i q[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) q[i] = afrag(i);
-    v8i p1 = bfrag(1);
+#pragma unroll
+    for (int t = 1; t < PF; ++t) pq[t] = bfrag(t);
     // FP8G: the rescale of block j-1 runs on the VALU between the MFMAs of
     // block j, which do not depend on it.
     v4f dprev[MB];
@@ -277,9 +293,9 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     };
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      v8i p2;
-      if (j + 2 < NB) p2 = bfrag(j + 2);
-      const v8i pb = p0;
+      v8i pnext;
+      if (j + PF < NB) pnext = bfrag(j + PF);
+      const v8i pb = pq[0];
       if (MODE == MODE_FP8G) {
         float sb4[4] = {0.f, 0.f, 0.f, 0.f};
         if (GN1) {
@@ -317,8 +333,9 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
           acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(phi, qhi, acc[j][i], 0, 0, 0);
         }
       }
-      p0 = p1;
-      if (j + 2 < NB) p1 = p2;
+#pragma unroll
+      for (int t = 0; t + 1 < PF; ++t) pq[t] = pq[t + 1];
+      if (j + PF < NB) pq[PF - 1] = pnext;
       if (MODE == MODE_FP8G && j > 0) {
         // issue order: the two prefetch reads, then one MFMA followed by
         // four rescale FMAs, MB times
@@ -333,10 +350,6 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     }
     if (MODE == MODE_FP8G) rescale(NB - 1, dprev, sb4p);
 
-    if (kScales) {
-#pragma unroll
-      for (int u = 0; u < SPT; ++u) lds_s[st ^ 1][tid + NT * u] = s_next[u];
-    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
