@@ -391,6 +391,177 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small and skinny products (few 256 x 256 tiles): split K inside the
+// workgroup.  SKW waves share one 64 x 64 output tile; wave w runs K-steps
+// [w * per, (w + 1) * per) over the whole tile, loading its own fragments
+// straight from global memory into registers (nothing is shared, so the
+// K loop has no barrier), next step's fragments in flight while the current
+// step is multiplied.  The SKW partial tiles then meet in LDS and each
+// output is the sum of the partials in wave order - the result does not
+// depend on timing.  Same MFMAs, scales and epilogue as k_gemm.
+constexpr int SK_T = 64;  // output tile edge
+constexpr int SKW = 4;    // waves (K slices) per workgroup
+
+template <int MODE, int OUT_BF16, int FA, int FB>
+__global__ void __launch_bounds__(64 * SKW, 1) k_gemm_sk(GemmArgs p) {
+  typedef typename std::conditional<MODE == MODE_I8, v4i, v4f>::type acc_t;
+  __shared__ __attribute__((aligned(16))) acc_t red[SKW][SK_T * SK_T / 4];
+
+  const int tid = threadIdx.x;
+  const int batch = blockIdx.z;
+  const int m0 = blockIdx.y * SK_T, n0 = blockIdx.x * SK_T;
+  const int M = p.M, N = p.N, K = p.K;
+  const int nk = K / BK;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int per = (nk + SKW - 1) / SKW;
+  const int k_begin = min(w * per, nk), k_end = min(k_begin + per, nk);
+
+  const uint8_t* A = p.A + int64_t(batch) * p.sA;
+  const uint8_t* B = p.B + int64_t(batch) * p.sB;
+  const int64_t a_bytes = int64_t(M) * K, b_bytes = int64_t(N) * K;
+  // lane offset inside a 16-row block: row r16, bytes 16 g (and +64)
+  const int voff = r16 * K + 16 * g;
+
+  // fragments of one K-step: f[0..3] A blocks (rows 16 i), f[4..7] B blocks
+  auto load_step = [&](int ks, v8i (&f)[8]) {
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint8_t* base = b < 4 ? A : B;
+      const int row0 = (b < 4 ? m0 : n0) + 16 * (b & 3);
+      const int64_t off = int64_t(row0) * K + int64_t(ks) * BK;
+      const int64_t rec = (b < 4 ? a_bytes : b_bytes) - off;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(base + off), (short)0,
+          int(rec < 0 ? 0 : (rec > 0x7FFFFFFF ? 0x7FFFFFFF : rec)), 0x00020000);
+      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64, 0, 0);
+      f[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // per-step scales of this lane: A rows 16 i + r16, B rows (MX) or group
+  auto load_scales = [&](int ks, float (&sa)[4], float& sb, int (&qa)[4], int (&qb)[4]) {
+    if (MODE == MODE_FP8G) {
+      const float* SA = static_cast<const float*>(p.SA) + int64_t(batch) * p.sSA;
+      const float* SB = static_cast<const float*>(p.SB) + int64_t(batch) * p.sSB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i] = SA[int64_t(min(m0 + 16 * i + r16, M - 1)) * nk + ks];
+      sb = SB[int64_t(n0 / 128) * nk + ks];
+    } else if (MODE == MODE_MX) {
+      const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + p.sSA * batch;
+      const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + p.sSB * batch;
+      const int kb = 4 * ks + g;  // this lane's 32-element block
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qa[i] = SA[int64_t(min(m0 + 16 * i + r16, M - 1)) * (K / 32) + kb];
+        qb[i] = SB[int64_t(min(n0 + 16 * i + r16, N - 1)) * (K / 32) + kb];
+      }
+    }
+  };
+
+  acc_t acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
+
+  if (k_begin < k_end) {
+    v8i cur[8], nxt[8];
+    float sa[4], sb = 0.f, na[4], nb = 0.f;
+    int qa[4], qb[4], nqa[4], nqb[4];
+    load_step(k_begin, cur);
+    load_scales(k_begin, sa, sb, qa, qb);
+    for (int ks = k_begin; ks < k_end; ++ks) {
+      const int kn = min(ks + 1, k_end - 1);  // the last step re-reads itself: no branch
+      load_step(kn, nxt);
+      load_scales(kn, na, nb, nqa, nqb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (MODE == MODE_FP8G) {
+            const v4f zero = {0.f, 0.f, 0.f, 0.f};
+            const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur[4 + j], cur[i], zero, 0, 0, 0, 0, 0, 0);
+            const float sc = sa[i] * sb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][i][r] = fmaf(d[r], sc, acc[j][i][r]);
+          } else if (MODE == MODE_MX) {
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur[4 + j], cur[i], acc[j][i], FB, FA,
+                                                                         0, qb[j], 0, qa[i]);
+          } else {
+            const v4i plo = {cur[4 + j][0], cur[4 + j][1], cur[4 + j][2], cur[4 + j][3]};
+            const v4i phi = {cur[4 + j][4], cur[4 + j][5], cur[4 + j][6], cur[4 + j][7]};
+            const v4i qlo = {cur[i][0], cur[i][1], cur[i][2], cur[i][3]};
+            const v4i qhi = {cur[i][4], cur[i][5], cur[i][6], cur[i][7]};
+            acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(plo, qlo, acc[j][i], 0, 0, 0);
+            acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(phi, qhi, acc[j][i], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) cur[b] = nxt[b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa[i] = na[i];
+        qa[i] = nqa[i];
+        qb[i] = nqb[i];
+      }
+      sb = nb;
+    }
+  }
+
+  // ---- the partial tiles meet in LDS: element (row, col) of wave w's
+  // partial at red[w][(row * 64 + col) / 4]; lane holds rows 16 i + r16,
+  // columns 16 j + 4 g .. + 3
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w][((16 * i + r16) * SK_T + 16 * j + 4 * g) / 4] = acc[j][i];
+  __syncthreads();
+
+  // 64 SKW threads share the 64 x 64 outputs: SKW threads per row, each
+  // summing CPT groups of 4 consecutive columns
+  constexpr int TPR = SKW;                // threads per row
+  constexpr int CPT = SK_T / TPR / 4;     // float4 groups per thread
+  static_assert(64 * SKW == SK_T * TPR, "one thread row per tile row");
+  const int row = tid / TPR, col0 = 4 * CPT * (tid % TPR);
+  const int m = m0 + row;
+  if (m >= M) return;
+  float xs = 0.f;
+  if (MODE == MODE_I8) xs = static_cast<const float*>(p.SA)[int64_t(batch) * p.sSA + m];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int col = col0 + 4 * c;
+    const int n = n0 + col;
+    if (n >= N) continue;
+    const int idx = (row * SK_T + col) / 4;
+    acc_t v = red[0][idx];
+#pragma unroll
+    for (int u = 1; u < SKW; ++u) v += red[u][idx];
+    const int64_t o = int64_t(batch) * p.sC + int64_t(m) * N + n;
+    float y[4];
+    if (MODE == MODE_I8) {
+      const float4 ws = *reinterpret_cast<const float4*>(static_cast<const float*>(p.SB) +
+                                                         int64_t(batch) * p.sSB + n);
+      const float wsv[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = float(v[r]) * (xs * wsv[r]);
+      if (p.acc_out != nullptr) *reinterpret_cast<int4*>(p.acc_out + o) = make_int4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = float(v[r]);
+    }
+    if (OUT_BF16) {
+      const uint32_t lo = encode_bf16(y[0]) | (encode_bf16(y[1]) << 16);
+      const uint32_t hi = encode_bf16(y[2]) | (encode_bf16(y[3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(y[0], y[1], y[2], y[3]);
+    }
+  }
+}
+
 __global__ void k_zero_bytes(uint32_t* __restrict__ p, int64_t n_words) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n_words; i += int64_t(gridDim.x) * 256)
     p[i] = 0u;
@@ -405,8 +576,18 @@ bsq_status zero_fill(void* p, int64_t bytes, hipStream_t st) {
   return launch_status("zero fill");
 }
 
+// Fewer 256 x 256 tiles than this and the split-K kernel is used instead
+// (the big-tile kernel would leave most of the 256 CUs idle).
+constexpr int64_t kSkinnyTiles = 64;
+
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
 bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
+  const int64_t tiles = int64_t((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * batch;
+  if (tiles < kSkinnyTiles && !GN1) {
+    dim3 grid(unsigned((a.N + SK_T - 1) / SK_T), unsigned((a.M + SK_T - 1) / SK_T), unsigned(batch));
+    hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB>), grid, 64 * SKW, 0, st, a);
+    return launch_status("gemm (split K)");
+  }
   constexpr int NW = 8;
   dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
   hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW>), grid, 64 * NW, 0, st, a);
