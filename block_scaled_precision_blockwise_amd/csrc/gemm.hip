@@ -94,49 +94,147 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-// NW waves per workgroup.  NW = 8: waves 4 (M) x 2 (N), each 64 x 128 (4 x 8
+// Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear
+// id and each XCD has its own L2, so the tiles one XCD receives should
+// share operand rows: linear id L goes to XCD L % 8 as its (L / 8)-th
+// workgroup; XCD x gets the x-th contiguous eighth of a tile order that
+// walks column-major through bands of kBand tile rows, i.e. a compact
+// block of tiles (4 x 8 for a 16 x 16 grid).
+__device__ __forceinline__ void tile_coords(int& tm, int& tn) {
+  constexpr int kBand = 4;
+  const int tiles_n = gridDim.x, tiles_m = gridDim.y;
+  const int T = tiles_n * tiles_m;
+  const int L = blockIdx.y * tiles_n + blockIdx.x;
+  const int per = T / 8;
+  const int t = (L < 8 * per) ? (L % 8) * per + L / 8 : L;
+  const int band = t / (kBand * tiles_n);
+  const int rows = min(kBand, tiles_m - band * kBand);
+  const int in = t - band * kBand * tiles_n;
+  tm = band * kBand + in % rows;
+  tn = in / rows;
+}
+
+// Epilogue of a 256 x 256 tile held by 8 waves as 64 x 128 wave tiles
+// (wave w: rows 64 (w % 4), columns 128 (w / 4)), through LDS.  A lane's
+// results are 4 columns of one row in 16 different rows per block, so
+// direct stores would write 16 row pieces of 64 bytes per instruction.
+// Instead each wave stages 32 of its 64 rows at a time in LDS (row-major,
+// kStageRowB bytes per row) and reads them back so that one store
+// instruction writes two whole 128-column rows.  The caller has finished
+// every LDS read and DMA of its main loop and passed a barrier, so the
+// stage buffers are free.
+constexpr int kStageRowB = 128 * 4 + 16;  // 128 floats + 16 B against bank conflicts
+constexpr int kLdsAB = 2 * (BM + BN) * BK > 8 * 32 * kStageRowB ? 2 * (BM + BN) * BK : 8 * 32 * kStageRowB;
+
+template <int MODE, int OUT_BF16, typename acc_t>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)[8][4], uint8_t* lds_ab, int w,
+                                           int lane, int batch, int m0, int n0) {
+  constexpr int MB = 4, NB = 8;
+  const int M = p.M, N = p.N;
+  const int wm = w & 3, wn = w >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  uint8_t* const stg = lds_ab + w * 32 * kStageRowB;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h > 0) __syncthreads();  // the first half has been read back
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+      const int m = m0 + 16 * MB * wm + 16 * i + r16;
+      float xs = 0.f;
+      if (MODE == MODE_I8) xs = static_cast<const float*>(p.SA)[int64_t(batch) * p.sSA + min(m, M - 1)];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + 128 * wn + 16 * j + 4 * g;
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        if (MODE == MODE_I8) {
+          if (n < N) {
+            const float4 ws = *reinterpret_cast<const float4*>(static_cast<const float*>(p.SB) +
+                                                               int64_t(batch) * p.sSB + n);
+            const float wsv[4] = {ws.x, ws.y, ws.z, ws.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = float(acc[j][i][r]) * (xs * wsv[r]);
+            if (p.acc_out != nullptr && m < M)
+              *reinterpret_cast<int4*>(p.acc_out + int64_t(batch) * p.sC + int64_t(m) * N + n) =
+                  make_int4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = float(acc[j][i][r]);
+        }
+        *reinterpret_cast<float4*>(stg + (16 * ii + r16) * kStageRowB + (16 * j + 4 * g) * 4) =
+            make_float4(y[0], y[1], y[2], y[3]);
+      }
+    }
+    __syncthreads();
+    // rows 32 h + rr of the wave's 64: lanes 0-31 one row, 32-63 the next.
+    // A tile inside the matrix stores without bounds checks, so that all
+    // 16 reads are issued before the first store.
+    auto put = [&](int t, const float4& v) {
+      const int rr = 2 * t + (lane >> 5), cc = 4 * (lane & 31);
+      const int m = m0 + 16 * MB * wm + 32 * h + rr;
+      const int n = n0 + 128 * wn + cc;
+      const int64_t o = int64_t(batch) * p.sC + int64_t(m) * N + n;
+      if (OUT_BF16) {
+        const uint32_t lo = encode_bf16(v.x) | (encode_bf16(v.y) << 16);
+        const uint32_t hi = encode_bf16(v.z) | (encode_bf16(v.w) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = v;
+      }
+    };
+    auto get = [&](int t) {
+      const int rr = 2 * t + (lane >> 5), cc = 4 * (lane & 31);
+      return *reinterpret_cast<const float4*>(stg + rr * kStageRowB + cc * 4);
+    };
+    if (m0 + BM <= M && n0 + BN <= N) {
+      float4 v[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) v[t] = get(t);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) put(t, v[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int rr = 2 * t + (lane >> 5), cc = 4 * (lane & 31);
+        const int m = m0 + 16 * MB * wm + 32 * h + rr;
+        const int n = n0 + 128 * wn + cc;
+        const float4 v = get(t);
+        if (m < M && n < N) put(t, v);
+      }
+    }
+  }
+}
+
+// NW = 8 waves per workgroup: waves 4 (M) x 2 (N), each 64 x 128 (4 x 8
 // blocks), accumulators in VGPRs - the FP8G rescale needs them on the VALU.
-// NW = 4: waves 2 x 2, each 128 x 128 (8 x 8 blocks); the MX and I8
-// accumulators never leave the matrix core's reach (AGPRs), and the larger
-// wave tile reads 1.5x fewer fragment bytes from LDS per MFMA.
+// (Measured alternatives that were not faster: 4 waves of 128 x 128 with
+// AGPR accumulators; two wave groups alternating between MFMA and memory
+// phases with a barrier per phase; an L2 prefetch two steps ahead.)
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW>
 __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
-  static_assert(NW == 8 || NW == 4, "4 or 8 waves");
-  static_assert(MODE != MODE_FP8G || NW == 8, "the FP8G rescale keeps its accumulators in VGPRs");
+  static_assert(NW == 8, "8 waves: the wave layout, scale staging and epilogue assume it");
   constexpr int NT = 64 * NW;          // threads
   constexpr int WGM = NW == 8 ? 4 : 2;  // waves along M
   constexpr int MB = BM / WGM / 16;     // 16-row blocks per wave along M
   constexpr int NB = 8;                 // 16-column blocks per wave along N
   constexpr int SPW = 32 / NW;          // 8-row DMA slices per wave per operand
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
-  // per-step scales: [0, 256) one word per A row, [256, 512) one per B row
-  // (MX, FP8G with GN1) or per 128-row B group (FP8G)
-  __shared__ uint32_t lds_s[2][512];
+  // LDS: the two A stages, then the two B stages; after the main loop the
+  // same bytes stage the epilogue
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ab[kLdsAB];
+  uint8_t* const lds_a = lds_ab;                // stage st at + st * BM * BK
+  uint8_t* const lds_b = lds_ab + 2 * BM * BK;  // stage st at + st * BN * BK
+  // scales of kSG consecutive K-steps: slot r < 256 holds A row r, slot
+  // 256 + r B row r (MX, FP8G with GN1) or B row group r (FP8G); the word of
+  // step ks sits at [(ks / kSG) & 1][slot * kSG + ks % kSG]
+  constexpr int kSG = 4;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][512 * kSG];
 
   const int tid = threadIdx.x;
   const int batch = blockIdx.z;
-  // Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear
-  // id and each XCD has its own L2, so the tiles one XCD receives should
-  // share operand rows: linear id L goes to XCD L % 8 as its (L / 8)-th
-  // workgroup; XCD x gets the x-th contiguous eighth of a tile order that
-  // walks column-major through bands of kBand tile rows, i.e. a compact
-  // block of tiles (4 x 8 for a 16 x 16 grid).
   int tm, tn;
-  {
-    constexpr int kBand = 4;
-    const int tiles_n = gridDim.x, tiles_m = gridDim.y;
-    const int T = tiles_n * tiles_m;
-    const int L = blockIdx.y * tiles_n + blockIdx.x;
-    const int per = T / 8;
-    const int t = (L < 8 * per) ? (L % 8) * per + L / 8 : L;
-    const int band = t / (kBand * tiles_n);
-    const int rows = min(kBand, tiles_m - band * kBand);
-    const int in = t - band * kBand * tiles_n;
-    tm = band * kBand + in % rows;
-    tn = in / rows;
-  }
+  tile_coords(tm, tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
@@ -158,25 +256,27 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   const int llog = (lane & 7) ^ (lrow & 7);
   const int voff = lrow * K + 16 * llog;  // < 8 NW K
   const int64_t a_bytes = int64_t(M) * K, b_bytes = int64_t(N) * K;
-  const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&lds_a[0][8 * w * BK]));
-  const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&lds_b[0][8 * w * BK]));
+  const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_a + 8 * w * BK));
+  const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_b + 8 * w * BK));
+  auto gload_slice = [&](int ks, int st, int s) {
+    const int64_t oa = int64_t(m0 + 8 * NW * s) * K + int64_t(ks) * BK;
+    const int64_t ob = int64_t(n0 + 8 * NW * s) * K + int64_t(ks) * BK;
+    const uint32_t soff = uint32_t(st * BM * BK + 8 * NW * s * BK);
+    lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + soff);
+    lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + soff);
+  };
   auto gload = [&](int ks, int st) {
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const int64_t oa = int64_t(m0 + 8 * NW * s) * K + int64_t(ks) * BK;
-      const int64_t ob = int64_t(n0 + 8 * NW * s) * K + int64_t(ks) * BK;
-      const uint32_t soff = uint32_t(st * BM * BK + 8 * NW * s * BK);
-      lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + soff);
-      lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + soff);
-    }
+    for (int s = 0; s < SPW; ++s) gload_slice(ks, st, s);
   };
 
-  // ---- per-step scales, by direct 4-byte buffer loads into LDS as well:
-  // slot r < 256 holds the step's word of A row r, slot 256 + r that of B
-  // row r (MX, FP8G with GN1) or of B row group r (FP8G).  Lane i of wave w
-  // fills slot 64 w + i (NW = 8: waves 0-3 the A rows, 4-7 the B rows).
-  // Lanes with nothing to move read row 0 of their operand's scales into a
-  // slot nobody reads.
+  // ---- scales, by direct 16-byte buffer loads into LDS as well: one load
+  // per row brings the words of kSG consecutive K-steps (one 16-byte piece
+  // of a scale row instead of one word of kSG of them), for the group of
+  // steps that follows the current one.
+  // Lane i of wave w fills slot 64 w + i (waves 0-3 the A rows, 4-7 the B
+  // rows).  Lanes with nothing to move read row 0 of their operand's scales
+  // into a slot nobody reads.
   constexpr bool kScales = MODE != MODE_I8;
   static_assert(!kScales || NW == 8, "scale staging assumes 512 threads");
   const uint8_t* sbase = nullptr;  // this wave's scale array at K-step 0
@@ -202,11 +302,15 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       soff_v = (a_side ? min(m0 + tid, M - 1) : min(n0 + r, N - 1)) * nk * 4;
     }
   }
-  const uint32_t ls_base = __builtin_amdgcn_readfirstlane(lds_addr_of(reinterpret_cast<const uint8_t*>(&lds_s[0][64 * w])));
-  auto sload = [&](int ks, int st) {
-    if (kScales)
-      lds_dma4(raw_rsrc(sbase + 4 * int64_t(ks), s_records - 4 * int64_t(ks)), soff_v,
-               ls_base + uint32_t(st * 512 * 4));
+  const uint32_t ls_base =
+      __builtin_amdgcn_readfirstlane(lds_addr_of(reinterpret_cast<const uint8_t*>(&lds_s[0][64 * w * kSG])));
+  // group q (steps kSG q .. kSG q + kSG - 1) into buffer q & 1; words past a
+  // row's last step are never read
+  auto sload = [&](int q) {
+    if (kScales) {
+      const int64_t o = 4 * int64_t(kSG) * q;
+      lds_dma16(raw_rsrc(sbase + o, s_records - o), soff_v, ls_base + uint32_t((q & 1) * 512 * kSG * 4));
+    }
   };
 
   // ---- wave / lane roles in the MFMA loop
@@ -223,7 +327,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     for (int i = 0; i < MB; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
 
   gload(0, 0);
-  sload(0, 0);
+  sload(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's direct loads have landed
   __syncthreads();
 
@@ -233,12 +337,14 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks & 1;
     const int kn = min(ks + 1, nk - 1);
+    // the next group's scales during the last step of this group (the
+    // buffer they go to was last read kSG steps ago)
+    if (ks % kSG == kSG - 1 && ks + 1 < nk) sload((ks + 1) / kSG);
     gload(kn, st ^ 1);
-    sload(kn, st ^ 1);
 
-    const uint8_t* ta = lds_a[st];
-    const uint8_t* tb = lds_b[st];
-    const uint32_t* ss = lds_s[st];
+    const uint8_t* ta = lds_a + st * BM * BK;
+    const uint8_t* tb = lds_b + st * BN * BK;
+    const uint32_t* ss = &lds_s[(ks / kSG) & 1][ks % kSG];  // + slot * kSG
     // LDS reads retire in order, so a wait for one read also waits for all
     // reads issued before it.  The step's scales are therefore read first,
     // then the fragments in the order their MFMAs need them (the first MFMA
@@ -257,13 +363,13 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     float sbg = 0.f;
     if (MODE == MODE_FP8G) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) sa[i] = __uint_as_float(ss[16 * MB * wm + 16 * i + r16]);
-      if (!GN1) sbg = __uint_as_float(ss[256 + wn]);
+      for (int i = 0; i < MB; ++i) sa[i] = __uint_as_float(ss[(16 * MB * wm + 16 * i + r16) * kSG]);
+      if (!GN1) sbg = __uint_as_float(ss[(256 + wn) * kSG]);
     } else if (MODE == MODE_MX) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) qa_w[i] = ss[16 * MB * wm + 16 * i + r16];
+      for (int i = 0; i < MB; ++i) qa_w[i] = ss[(16 * MB * wm + 16 * i + r16) * kSG];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) qb_w[j] = ss[256 + 128 * wn + 16 * j + r16];
+      for (int j = 0; j < NB; ++j) qb_w[j] = ss[(256 + 128 * wn + 16 * j + r16) * kSG];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the scale reads ahead of the fragment reads
     constexpr int PF = 2;  // B fragments in flight ahead of their MFMAs
@@ -299,9 +405,8 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       if (MODE == MODE_FP8G) {
         float sb4[4] = {0.f, 0.f, 0.f, 0.f};
         if (GN1) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&ss[256 + 128 * wn + 16 * j + 4 * g]);
-          sb4[0] = __uint_as_float(v.x); sb4[1] = __uint_as_float(v.y);
-          sb4[2] = __uint_as_float(v.z); sb4[3] = __uint_as_float(v.w);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sb4[r] = __uint_as_float(ss[(256 + 128 * wn + 16 * j + 4 * g + r) * kSG]);
         }
         v4f dcur[MB];
 #pragma unroll
@@ -354,41 +459,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     __syncthreads();
   }
 
-  // ---- epilogue
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + 16 * MB * wm + 16 * i + r16;
-    if (m >= M) continue;
-    float xs = 0.f;
-    if (MODE == MODE_I8) xs = static_cast<const float*>(p.SA)[int64_t(batch) * p.sSA + m];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int n = n0 + 128 * wn + 16 * j + 4 * g;
-      if (n >= N) continue;
-      const int64_t o = int64_t(batch) * p.sC + int64_t(m) * N + n;
-      float y[4];
-      if (MODE == MODE_I8) {
-        const float4 ws = *reinterpret_cast<const float4*>(static_cast<const float*>(p.SB) +
-                                                           int64_t(batch) * p.sSB + n);
-        const float wsv[4] = {ws.x, ws.y, ws.z, ws.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = float(acc[j][i][r]) * (xs * wsv[r]);
-        if (p.acc_out != nullptr)
-          *reinterpret_cast<int4*>(p.acc_out + o) =
-              make_int4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = float(acc[j][i][r]);
-      }
-      if (OUT_BF16) {
-        const uint32_t lo = encode_bf16(y[0]) | (encode_bf16(y[1]) << 16);
-        const uint32_t hi = encode_bf16(y[2]) | (encode_bf16(y[3]) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(y[0], y[1], y[2], y[3]);
-      }
-    }
-  }
+  store_tile<MODE, OUT_BF16>(p, acc, lds_ab, w, lane, batch, m0, n0);
 }
 
 // ---------------------------------------------------------------------------
