@@ -2,8 +2,16 @@
 //
 // All of them are bound by HBM: one streaming read of the input, one write
 // of the codes.  Blocks are reduced inside a wavefront with cross-lane
-// shuffles; per-element division is a true IEEE float32 division (the
-// pages divide by the scale), never a reciprocal multiply.
+// shuffles.  The pages divide each value by the block scale; the code is
+// that of the correctly rounded float32 quotient x / s, obtained without a
+// division per element: with r = 1 / s correctly rounded, q0 = x * r is
+// within an ulp of x / s, the residual x - q0 * s is exact in one FMA, and
+// q0 + (x - q0 * s) * r rounds to the correctly rounded quotient whenever
+// nothing underflows (Markstein's theorem on division by a correctly
+// rounded reciprocal).  Quotients below 2^-11 - where underflow can occur -
+// only ever encode to a zero of x's sign, and are returned as that zero.
+// float32 -> fp8 uses the gfx950 conversion instructions (nearest, ties to
+// even; inputs already clamped to the format's range).
 #include "common.h"
 #include "quant.h"
 
@@ -30,12 +38,28 @@ __device__ __forceinline__ float fp8_block_scale(float amax) {
   return fmaxf(amax / kE4M3Max, scale_floor());
 }
 
-__device__ __forceinline__ uint32_t quant4_e4m3(float4 v, float s) {
-  auto q = [s](float x) {
-    const float y = fminf(fmaxf(x / s, -kE4M3Max), kE4M3Max);
-    return encode_e4m3(y);
-  };
-  return q(v.x) | (q(v.y) << 8) | (q(v.z) << 16) | (q(v.w) << 24);
+// Four float32 in [-fmax, fmax] to four fp8 codes (first value in the low
+// byte), nearest with ties to even.
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+__device__ __forceinline__ uint32_t cvt4_e5m2(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+  return uint32_t(__builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true));
+}
+
+// x / s correctly rounded for |x / s| >= 2^-11, a zero of x's sign below
+// (r = 1 / s correctly rounded, s > 0 normal).
+__device__ __forceinline__ float quot(float x, float s, float r) {
+  const float q0 = x * r;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+  return fabsf(q0) < 0x1p-11f ? __builtin_copysignf(0.0f, x) : q1;
+}
+
+__device__ __forceinline__ uint32_t quant4_e4m3(float4 v, float s, float r) {
+  auto q = [s, r](float x) { return fminf(fmaxf(quot(x, s, r), -kE4M3Max), kE4M3Max); };
+  return cvt4_e4m3(q(v.x), q(v.y), q(v.z), q(v.w));
 }
 
 // ------------------------------------------------ fp8 1 x G row blocks ----
@@ -59,8 +83,9 @@ __global__ void __launch_bounds__(256) k_fp8_rowblock(const float4* __restrict__
       const int64_t f = base + u * 256 + threadIdx.x;
       const float amax = group_max<LPB>(amax4(v[u]));
       const float s = fp8_block_scale(amax);
+      const float r = 1.0f / s;
       if (f < n4) {
-        codes[f] = quant4_e4m3(v[u], s);
+        codes[f] = quant4_e4m3(v[u], s, r);
         if ((threadIdx.x % LPB) == 0) scales[f / LPB] = s;
       }
     }
@@ -92,10 +117,11 @@ __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ s
   __syncthreads();
   const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float s = fp8_block_scale(amax);
+  const float r = 1.0f / s;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     uint32_t* q = reinterpret_cast<uint32_t*>(codes + (row0 + r0 + 8 * i) * cols + col0);
-    *q = quant4_e4m3(v[i], s);
+    *q = quant4_e4m3(v[i], s, r);
   }
   if (tx == 0) scales[int64_t(blockIdx.y) * gridDim.x + blockIdx.x] = s;
 }
@@ -112,11 +138,14 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return min(max(E, -127), 127);
 }
 
+// x * 2^-E (exact) clamped to the format's range, four at a time.
 template <int CODE>  // 0 = e4m3, 1 = e5m2
-__device__ __forceinline__ uint32_t mx_encode(float x, int E) {
-  const float y = ldexpf(x, -E);
-  if (CODE == 0) return encode_e4m3(fminf(fmaxf(y, -kE4M3Max), kE4M3Max));
-  return encode_e5m2(fminf(fmaxf(y, -kE5M2Max), kE5M2Max));
+__device__ __forceinline__ uint32_t mx_encode4(const float* x, int E) {
+  constexpr float fmax = CODE == 0 ? kE4M3Max : kE5M2Max;
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = fminf(fmaxf(ldexpf(x[i], -E), -fmax), fmax);
+  return CODE == 0 ? cvt4_e4m3(y[0], y[1], y[2], y[3]) : cvt4_e5m2(y[0], y[1], y[2], y[3]);
 }
 
 // Loads 8 consecutive source values as float (from f32 or bf16).
@@ -168,13 +197,7 @@ __global__ void __launch_bounds__(256) k_mx_rows(const void* __restrict__ src,
       m = group_max<4>(m);
       const int E = mx_exponent<EMAX>(m);
       if (f < n8) {
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo |= mx_encode<CODE>(x[u][i], E) << (8 * i);
-          hi |= mx_encode<CODE>(x[u][4 + i], E) << (8 * i);
-        }
-        codes[f] = make_uint2(lo, hi);
+        codes[f] = make_uint2(mx_encode4<CODE>(&x[u][0], E), mx_encode4<CODE>(&x[u][4], E));
         if ((threadIdx.x & 3) == 0) scales[f >> 2] = uint8_t(E + 127);
       }
     }
@@ -225,11 +248,7 @@ __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
   if (orow < cols && ocol < rows) {
     uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[q] = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[q] |= mx_encode<CODE>(x[4 * q + i], E) << (8 * i);
-    }
+    for (int q = 0; q < 4; ++q) w[q] = mx_encode4<CODE>(&x[4 * q], E);
     *reinterpret_cast<uint4*>(codes + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
     if ((seg & 1) == 0) scales[orow * (rows / 32) + (ocol >> 5)] = uint8_t(E + 127);
   }
@@ -241,14 +260,14 @@ __device__ __forceinline__ float int8_scale(float amax) {
   return amax == 0.f ? 1.0f : amax / 127.0f;
 }
 
-__device__ __forceinline__ int32_t int8_code(float x, float s) {
-  const float r = __builtin_rintf(x / s);
-  return int32_t(fminf(fmaxf(r, -127.f), 127.f));
+// round(x / s) with ties to even, clamped to +-127 (r = 1 / s).
+__device__ __forceinline__ int32_t int8_code(float x, float s, float r) {
+  return int32_t(fminf(fmaxf(__builtin_rintf(quot(x, s, r)), -127.f), 127.f));
 }
 
-__device__ __forceinline__ uint32_t int8_pack4(float4 v, float s) {
-  return (uint32_t(int8_code(v.x, s)) & 0xFFu) | ((uint32_t(int8_code(v.y, s)) & 0xFFu) << 8) |
-         ((uint32_t(int8_code(v.z, s)) & 0xFFu) << 16) | ((uint32_t(int8_code(v.w, s)) & 0xFFu) << 24);
+__device__ __forceinline__ uint32_t int8_pack4(float4 v, float s, float r) {
+  return (uint32_t(int8_code(v.x, s, r)) & 0xFFu) | ((uint32_t(int8_code(v.y, s, r)) & 0xFFu) << 8) |
+         ((uint32_t(int8_code(v.z, s, r)) & 0xFFu) << 16) | ((uint32_t(int8_code(v.w, s, r)) & 0xFFu) << 24);
 }
 
 template <int N>
@@ -282,11 +301,12 @@ __global__ void __launch_bounds__(256) k_int8_rows_vec(const float* __restrict__
     m = fmaxf(m, amax4(v[i]));
   }
   const float s = int8_scale(block_max<4>(m, red));
+  const float r = 1.0f / s;
   uint32_t* out = xq + int64_t(blockIdx.x) * d4;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int64_t c = threadIdx.x + 256 * i;
-    if (c < d4) out[c] = int8_pack4(v[i], s);
+    if (c < d4) out[c] = int8_pack4(v[i], s, r);
   }
   if (threadIdx.x == 0) xs[blockIdx.x] = s;
 }
@@ -300,8 +320,9 @@ __global__ void __launch_bounds__(256) k_int8_rows_any(const float* __restrict__
   float m = 0.f;
   for (int64_t c = threadIdx.x; c < D; c += 256) m = fmaxf(m, fabsf(row[c]));
   const float s = int8_scale(block_max<4>(m, red));
+  const float r = 1.0f / s;
   int8_t* out = xq + int64_t(blockIdx.x) * D;
-  for (int64_t c = threadIdx.x; c < D; c += 256) out[c] = int8_t(int8_code(row[c], s));
+  for (int64_t c = threadIdx.x; c < D; c += 256) out[c] = int8_t(int8_code(row[c], s, r));
   if (threadIdx.x == 0) xs[blockIdx.x] = s;
 }
 
@@ -393,11 +414,12 @@ __global__ void __launch_bounds__(256) k_int8_cols_quant(const float* __restrict
   const int cx = tx & 31;                         // 4 columns each
   const int rr = tx >> 5;                         // 8 row phases
   const bool vec = (D_out % 4) == 0;
-  float s[4];
+  float s[4], rs[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t j = j0 + 4 * cx + q;
     s[q] = j < D_out ? int8_scale(__uint_as_float(cmax[j])) : 1.0f;
+    rs[q] = 1.0f / s[q];
   }
   for (int k = 0; k < 16; ++k) {
     const int r = rr + 8 * k;
@@ -409,13 +431,13 @@ __global__ void __launch_bounds__(256) k_int8_cols_quant(const float* __restrict
         const float4 v = ldnt(reinterpret_cast<const float4*>(w + i * D_out + j));
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) packed |= (uint32_t(int8_code(vv[q], s[q])) & 0xFFu) << (8 * q);
+        for (int q = 0; q < 4; ++q) packed |= (uint32_t(int8_code(vv[q], s[q], rs[q])) & 0xFFu) << (8 * q);
         *reinterpret_cast<uint32_t*>(wq + i * D_out + j) = packed;
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (j + q < D_out) {
-            const int32_t c = int8_code(w[i * D_out + j + q], s[q]);
+            const int32_t c = int8_code(w[i * D_out + j + q], s[q], rs[q]);
             wq[i * D_out + j + q] = int8_t(c);
             packed |= (uint32_t(c) & 0xFFu) << (8 * q);
           }
