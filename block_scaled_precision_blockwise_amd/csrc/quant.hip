@@ -356,23 +356,28 @@ __global__ void __launch_bounds__(256) k_int8_colmax_vec(const float4* __restric
   const int64_t r_end = min(r_begin + rows_per_wg, D_in);
   float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < d4) {
+    // rows r_begin + ph + 4 n; 16 loads in flight per thread when the
+    // workgroup's 64 rows are all there
     int64_t r = r_begin + ph;
-    for (; r + 12 < r_end; r += 16) {
-      const float4 a = ldnt(w + r * d4 + c);
-      const float4 b = ldnt(w + (r + 4) * d4 + c);
-      const float4 e = ldnt(w + (r + 8) * d4 + c);
-      const float4 f = ldnt(w + (r + 12) * d4 + c);
-      m.x = fmaxf(fmaxf(m.x, fmaxf(fabsf(a.x), fabsf(b.x))), fmaxf(fabsf(e.x), fabsf(f.x)));
-      m.y = fmaxf(fmaxf(m.y, fmaxf(fabsf(a.y), fabsf(b.y))), fmaxf(fabsf(e.y), fabsf(f.y)));
-      m.z = fmaxf(fmaxf(m.z, fmaxf(fabsf(a.z), fabsf(b.z))), fmaxf(fabsf(e.z), fabsf(f.z)));
-      m.w = fmaxf(fmaxf(m.w, fmaxf(fabsf(a.w), fabsf(b.w))), fmaxf(fabsf(e.w), fabsf(f.w)));
-    }
-    for (; r < r_end; r += 4) {
-      const float4 a = ldnt(w + r * d4 + c);
-      m.x = fmaxf(m.x, fabsf(a.x));
-      m.y = fmaxf(m.y, fabsf(a.y));
-      m.z = fmaxf(m.z, fabsf(a.z));
-      m.w = fmaxf(m.w, fabsf(a.w));
+    if (rows_per_wg == 64 && r_begin + 64 <= r_end) {
+      float4 a[16];
+#pragma unroll
+      for (int n = 0; n < 16; ++n) a[n] = ldnt(w + (r + 4 * n) * d4 + c);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        m.x = fmaxf(m.x, fabsf(a[n].x));
+        m.y = fmaxf(m.y, fabsf(a[n].y));
+        m.z = fmaxf(m.z, fabsf(a[n].z));
+        m.w = fmaxf(m.w, fabsf(a[n].w));
+      }
+    } else {
+      for (; r < r_end; r += 4) {
+        const float4 a = ldnt(w + r * d4 + c);
+        m.x = fmaxf(m.x, fabsf(a.x));
+        m.y = fmaxf(m.y, fabsf(a.y));
+        m.z = fmaxf(m.z, fabsf(a.z));
+        m.w = fmaxf(m.w, fabsf(a.w));
+      }
     }
   }
   part[ph][cx] = m;
@@ -401,73 +406,89 @@ __global__ void __launch_bounds__(256) k_fill_u32(uint32_t* __restrict__ p, int6
 
 // Codes of w with the column scales derived from the column maxima; also
 // the transposed codes w_qT[D_out, D_in] when requested.  Tiles of 128 x
-// 128 (D_in x D_out) through LDS; any sizes (edges guarded).
+// 128 (D_in x D_out); any sizes (edges guarded).  Thread (cx, rg) owns
+// columns 4 cx .. 4 cx + 3 and the four runs of 4 consecutive rows
+// 4 (rg + 8 kk) .. + 3, kk = 0..3; all 16 row loads are issued first.  For
+// the transpose, a column's 4 codes of one run form one word in LDS
+// (tq[column][row / 4]), read back 16 bytes at a time.
 __global__ void __launch_bounds__(256) k_int8_cols_quant(const float* __restrict__ w,
                                                          const uint32_t* __restrict__ cmax,
                                                          int8_t* __restrict__ wq,
                                                          int8_t* __restrict__ wqT, int64_t D_in,
                                                          int64_t D_out) {
-  __shared__ uint8_t tq[128][128 + 16];
+  __shared__ __attribute__((aligned(16))) uint32_t tq[128][36];  // 144-byte rows
   const int tx = threadIdx.x;
   const int64_t i0 = int64_t(blockIdx.y) * 128;  // rows of w (D_in)
   const int64_t j0 = int64_t(blockIdx.x) * 128;  // cols of w (D_out)
-  const int cx = tx & 31;                         // 4 columns each
-  const int rr = tx >> 5;                         // 8 row phases
-  const bool vec = (D_out % 4) == 0;
+  const int cx = tx & 31;
+  const int rg = tx >> 5;
+  const int64_t j = j0 + 4 * cx;
+  const bool vec = (D_out % 4) == 0 && j < D_out;
   float s[4], rs[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int64_t j = j0 + 4 * cx + q;
-    s[q] = j < D_out ? int8_scale(__uint_as_float(cmax[j])) : 1.0f;
+    s[q] = j + q < D_out ? int8_scale(__uint_as_float(cmax[j + q])) : 1.0f;
     rs[q] = 1.0f / s[q];
   }
-  for (int k = 0; k < 16; ++k) {
-    const int r = rr + 8 * k;
-    const int64_t i = i0 + r;
-    const int64_t j = j0 + 4 * cx;
-    uint32_t packed = 0;
+  float4 v[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    const int64_t i = i0 + 4 * (rg + 8 * (n >> 2)) + (n & 3);
+    v[n] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i < D_in) {
-      if (vec && j < D_out) {
-        const float4 v = ldnt(reinterpret_cast<const float4*>(w + i * D_out + j));
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) packed |= (uint32_t(int8_code(vv[q], s[q], rs[q])) & 0xFFu) << (8 * q);
-        *reinterpret_cast<uint32_t*>(wq + i * D_out + j) = packed;
+      if (vec) {
+        v[n] = ldnt(reinterpret_cast<const float4*>(w + i * D_out + j));
       } else {
+        float e[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (j + q < D_out) {
-            const int32_t c = int8_code(w[i * D_out + j + q], s[q], rs[q]);
-            wq[i * D_out + j + q] = int8_t(c);
-            packed |= (uint32_t(c) & 0xFFu) << (8 * q);
-          }
-        }
+        for (int q = 0; q < 4; ++q)
+          if (j + q < D_out) e[q] = w[i * D_out + j + q];
+        v[n] = make_float4(e[0], e[1], e[2], e[3]);
       }
     }
+  }
+  uint32_t packed[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) tq[4 * cx + q][r] = uint8_t(packed >> (8 * q));
+  for (int n = 0; n < 16; ++n) {
+    const int64_t i = i0 + 4 * (rg + 8 * (n >> 2)) + (n & 3);
+    const float vv[4] = {v[n].x, v[n].y, v[n].z, v[n].w};
+    packed[n] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) packed[n] |= (uint32_t(int8_code(vv[q], s[q], rs[q])) & 0xFFu) << (8 * q);
+    if (i < D_in) {
+      if (vec) {
+        *reinterpret_cast<uint32_t*>(wq + i * D_out + j) = packed[n];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (j + q < D_out) wq[i * D_out + j + q] = int8_t(packed[n] >> (8 * q));
+      }
+    }
   }
   if (wqT == nullptr) return;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) word |= ((packed[4 * kk + t] >> (8 * q)) & 0xFFu) << (8 * t);
+      tq[4 * cx + q][rg + 8 * kk] = word;
+    }
   __syncthreads();
   // 128 output rows (j) x 128 bytes (i): thread writes 64 bytes of one row
   const int oj = tx >> 1, half = tx & 1;
-  const int64_t j = j0 + oj;
-  if (j >= D_out) return;
+  const int64_t jo = j0 + oj;
+  if (jo >= D_out) return;
   const int64_t ib = i0 + 64 * half;
-  int8_t* dst = wqT + j * D_in + ib;
+  int8_t* dst = wqT + jo * D_in + ib;
   if ((D_in % 16) == 0 && ib + 64 <= D_in) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint8_t* srow = &tq[oj][64 * half + 16 * q];
-      uint4 pk;
-      pk.x = srow[0] | (srow[1] << 8) | (srow[2] << 16) | (uint32_t(srow[3]) << 24);
-      pk.y = srow[4] | (srow[5] << 8) | (srow[6] << 16) | (uint32_t(srow[7]) << 24);
-      pk.z = srow[8] | (srow[9] << 8) | (srow[10] << 16) | (uint32_t(srow[11]) << 24);
-      pk.w = srow[12] | (srow[13] << 8) | (srow[14] << 16) | (uint32_t(srow[15]) << 24);
-      *reinterpret_cast<uint4*>(dst + 16 * q) = pk;
-    }
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(dst + 16 * q) = *reinterpret_cast<const uint4*>(&tq[oj][16 * half + 4 * q]);
   } else {
-    for (int q = 0; q < 64 && ib + q < D_in; ++q) dst[q] = int8_t(tq[oj][64 * half + q]);
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(&tq[oj][0]);
+    for (int q = 0; q < 64 && ib + q < D_in; ++q) dst[q] = int8_t(row[64 * half + q]);
   }
 }
 
