@@ -114,11 +114,11 @@ __device__ __forceinline__ void tile_coords(int& tm, int& tn) {
   tn = in / rows;
 }
 
-// Epilogue of a 256 x 256 tile held by 8 waves as 64 x 128 wave tiles
-// (wave w: rows 64 (w % 4), columns 128 (w / 4)), through LDS.  A lane's
+// Epilogue of a (64 MB) x 256 tile held by 8 waves as (16 MB) x 128 wave
+// tiles (wave w: rows 16 MB (w % 4), columns 128 (w / 4)), through LDS.  A lane's
 // results are 4 columns of one row in 16 different rows per block, so
 // direct stores would write 16 row pieces of 64 bytes per instruction.
-// Instead each wave stages 32 of its 64 rows at a time in LDS (row-major,
+// Instead each wave stages 32 of its rows at a time in LDS (row-major,
 // kStageRowB bytes per row) and reads them back so that one store
 // instruction writes two whole 128-column rows.  The caller has finished
 // every LDS read and DMA of its main loop and passed a barrier, so the
@@ -126,16 +126,17 @@ __device__ __forceinline__ void tile_coords(int& tm, int& tn) {
 constexpr int kStageRowB = 128 * 4 + 16;  // 128 floats + 16 B against bank conflicts
 constexpr int kLdsAB = 2 * (BM + BN) * BK > 8 * 32 * kStageRowB ? 2 * (BM + BN) * BK : 8 * 32 * kStageRowB;
 
-template <int MODE, int OUT_BF16, typename acc_t>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)[8][4], uint8_t* lds_ab, int w,
+template <int MODE, int OUT_BF16, int MB, typename acc_t>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)[8][MB], uint8_t* lds_ab, int w,
                                            int lane, int batch, int m0, int n0) {
-  constexpr int MB = 4, NB = 8;
+  constexpr int NB = 8;
+  static_assert(MB == 2 || MB == 4, "32 or 64 rows per wave");
   const int M = p.M, N = p.N;
   const int wm = w & 3, wn = w >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   uint8_t* const stg = lds_ab + w * 32 * kStageRowB;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < MB / 2; ++h) {
     if (h > 0) __syncthreads();  // the first half has been read back
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
@@ -175,19 +176,21 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
       const int m = m0 + 16 * MB * wm + 32 * h + rr;
       const int n = n0 + 128 * wn + cc;
       const int64_t o = int64_t(batch) * p.sC + int64_t(m) * N + n;
+      // streaming stores: the output is not read again by this kernel
       if (OUT_BF16) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const uint32_t lo = encode_bf16(v.x) | (encode_bf16(v.y) << 16);
         const uint32_t hi = encode_bf16(v.z) | (encode_bf16(v.w) << 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(lo, hi);
+        __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p.out) + o));
       } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = v;
+        __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + o));
       }
     };
     auto get = [&](int t) {
       const int rr = 2 * t + (lane >> 5), cc = 4 * (lane & 31);
       return *reinterpret_cast<const float4*>(stg + rr * kStageRowB + cc * 4);
     };
-    if (m0 + BM <= M && n0 + BN <= N) {
+    if (m0 + 64 * MB <= M && n0 + BN <= N) {
       float4 v[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) v[t] = get(t);
@@ -211,20 +214,22 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
 // (Measured alternatives that were not faster: 4 waves of 128 x 128 with
 // AGPR accumulators; two wave groups alternating between MFMA and memory
 // phases with a barrier per phase; an L2 prefetch two steps ahead.)
-template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW>
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM>
 __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   static_assert(NW == 8, "8 waves: the wave layout, scale staging and epilogue assume it");
+  static_assert(TBM == 256 || TBM == 128, "tile rows");
   constexpr int NT = 64 * NW;          // threads
-  constexpr int WGM = NW == 8 ? 4 : 2;  // waves along M
-  constexpr int MB = BM / WGM / 16;     // 16-row blocks per wave along M
+  constexpr int WGM = 4;                // waves along M
+  constexpr int MB = TBM / WGM / 16;    // 16-row blocks per wave along M
   constexpr int NB = 8;                 // 16-column blocks per wave along N
-  constexpr int SPW = 32 / NW;          // 8-row DMA slices per wave per operand
+  constexpr int SPW = 32 / NW;          // 8-row DMA slices per wave of B
+  constexpr int SPWA = TBM / 8 / NW;    // 8-row DMA slices per wave of A
 
   // LDS: the two A stages, then the two B stages; after the main loop the
   // same bytes stage the epilogue
   __shared__ __attribute__((aligned(16))) uint8_t lds_ab[kLdsAB];
-  uint8_t* const lds_a = lds_ab;                // stage st at + st * BM * BK
-  uint8_t* const lds_b = lds_ab + 2 * BM * BK;  // stage st at + st * BN * BK
+  uint8_t* const lds_a = lds_ab;                 // stage st at + st * TBM * BK
+  uint8_t* const lds_b = lds_ab + 2 * TBM * BK;  // stage st at + st * BN * BK
   // scales of kSG consecutive K-steps: slot r < 256 holds A row r, slot
   // 256 + r B row r (MX, FP8G with GN1) or B row group r (FP8G); the word of
   // step ks sits at [(ks / kSG) & 1][slot * kSG + ks % kSG]
@@ -235,7 +240,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   const int batch = blockIdx.z;
   int tm, tn;
   tile_coords(tm, tn);
-  const int m0 = tm * BM;
+  const int m0 = tm * TBM;
   const int n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
   const int nk = K / BK;
@@ -259,11 +264,12 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_a + 8 * w * BK));
   const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_b + 8 * w * BK));
   auto gload_slice = [&](int ks, int st, int s) {
-    const int64_t oa = int64_t(m0 + 8 * NW * s) * K + int64_t(ks) * BK;
+    if (s < SPWA) {
+      const int64_t oa = int64_t(m0 + 8 * NW * s) * K + int64_t(ks) * BK;
+      lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + uint32_t(st * TBM * BK + 8 * NW * s * BK));
+    }
     const int64_t ob = int64_t(n0 + 8 * NW * s) * K + int64_t(ks) * BK;
-    const uint32_t soff = uint32_t(st * BM * BK + 8 * NW * s * BK);
-    lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + soff);
-    lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + soff);
+    lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + uint32_t(st * BN * BK + 8 * NW * s * BK));
   };
   auto gload = [&](int ks, int st) {
 #pragma unroll
@@ -342,7 +348,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     if (ks % kSG == kSG - 1 && ks + 1 < nk) sload((ks + 1) / kSG);
     gload(kn, st ^ 1);
 
-    const uint8_t* ta = lds_a + st * BM * BK;
+    const uint8_t* ta = lds_a + st * TBM * BK;
     const uint8_t* tb = lds_b + st * BN * BK;
     const uint32_t* ss = &lds_s[(ks / kSG) & 1][ks % kSG];  // + slot * kSG
     // LDS reads retire in order, so a wait for one read also waits for all
@@ -459,7 +465,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     __syncthreads();
   }
 
-  store_tile<MODE, OUT_BF16>(p, acc, lds_ab, w, lane, batch, m0, n0);
+  store_tile<MODE, OUT_BF16, MB>(p, acc, lds_ab, w, lane, batch, m0, n0);
 }
 
 // ---------------------------------------------------------------------------
@@ -647,6 +653,11 @@ bsq_status zero_fill(void* p, int64_t bytes, hipStream_t st) {
   return launch_status("zero fill");
 }
 
+// Up to this many 256 x 256 tiles (and at least kSkinnyTiles), the big
+// kernel runs on 256 x 128-row tiles instead: twice the workgroups, which
+// still fit one pass over the 256 CUs, for 1.5x the operand bytes per flop.
+constexpr int64_t kHalfTiles = 134;
+
 // Fewer 256 x 256 tiles than this and the split-K kernel is used instead
 // (the big-tile kernel would leave most of the 256 CUs idle).
 constexpr int64_t kSkinnyTiles = 64;
@@ -660,8 +671,14 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
     return launch_status("gemm (split K)");
   }
   constexpr int NW = 8;
-  dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
-  hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW>), grid, 64 * NW, 0, st, a);
+  if (tiles <= kHalfTiles) {
+    // doubling the tile count still fits one pass over the CUs: 128-row tiles
+    dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + 127) / 128), unsigned(batch));
+    hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 128>), grid, 64 * NW, 0, st, a);
+  } else {
+    dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
+    hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 256>), grid, 64 * NW, 0, st, a);
+  }
   return launch_status("gemm");
 }
 

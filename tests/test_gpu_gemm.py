@@ -375,3 +375,34 @@ def test_backward_full_size_sampled():
     yr, T = OM.scaled_matmul(a[None], b[None], sa[None], sb[None], "e5m2", "e5m2", "e8m0")
     assert_within_T(dWh[nrows], yr[0], T[0], "dW rows", bf16=True)
     assert np.all(np.isfinite(dXh)) and np.all(np.isfinite(dWh))
+
+
+# ------------------------------------------------- 128-row tile variant ---
+# Products with 64..134 tiles of 256 x 256 run on 256 x 128-row tiles; these
+# shapes land there, with a ragged last tile row.
+
+def test_half_tiles_blockwise():
+    M, N, K = 1900, 4096, 256
+    say("blockwise on 128-row tiles", M, N, K)
+    a, b, sa, sb = _recipe_blockwise(M, N, K, 950)
+    y = _run_blockwise(a, b, sa, sb)
+    yr, T = OM.blockwise_fp8(a, b, sa, sb)
+    assert_within_T(host(y), yr, T, "y")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_half_tiles_mx(out):
+    torch = _torch()
+    Bt, M, N, K = 2, 1100, 2048, 256
+    say("scaled_matmul mx on 128-row tiles", Bt, M, N, K, out)
+    a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 961), "e4m3")
+    b, _ = OQ.mx(synth.randn_f32((Bt, N, K), 962), "e4m3")
+    sa = synth.random_e8m0_codes((Bt, M, K // 32), 963)
+    sb = synth.random_e8m0_codes((Bt, N, K // 32), 964)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = filled((Bt, M, N), od, float("nan"))
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=bsq.BSQ_E4M3,
+                          rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_E8M0)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, "e4m3", "e4m3", "e8m0")
+    yh = host(y) if out == "f32" else OF.decode_bf16(host(y))
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
