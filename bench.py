@@ -43,6 +43,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PAGE_T_PROD_TFLOPS_4096 = 2 * 4096 ** 3 / 1.06e-3 / 1e12
 GEMM_SRC = os.path.join(ROOT, "block_scaled_precision_blockwise_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_4096_traffic.json")
+DEFAULT_SUITE_OUT = os.path.join(ROOT, "gpurun_out", "suite.jsonl")
 
 
 def _log(*a):
@@ -397,13 +398,88 @@ def run_suite(args):
     _log(f"[suite] wrote {len(rows)} rows to {out_path}")
 
 
+# The block_scaled_mm page's shape table ("Shapes"): m, n, k (group 128 x
+# 128), and its T_SOL (XPU-A) and T_Prod in microseconds - another
+# machine's figures, quoted beside ours as context.
+PAGE_SWEEP = [
+    (349, 2048, 2048, 6.36, 61.80), (1024, 2048, 2048, 18.67, 73.90),
+    (4533, 2048, 2048, 82.66, 300.00), (6918, 2048, 2048, 126.15, 440.40),
+    (20480, 2048, 2048, 373.46, 1240.0), (51200, 2048, 2048, 933.65, 3100.0),
+    (65536, 2048, 2048, 1200.0, 3970.0), (98304, 2048, 2048, 1790.0, 5930.0),
+    (118784, 2048, 2048, 2170.0, 7180.0), (250880, 2048, 2048, 4570.0, 15130.0),
+    (516096, 2048, 2048, 9410.0, 31140.0), (704512, 2048, 2048, 12850.0, 42520.0),
+    (237, 4096, 4096, 17.29, 118.30), (3072, 4096, 4096, 224.10, 801.90),
+    (4096, 4096, 4096, 298.80, 1060.0), (8192, 4096, 4096, 597.60, 2090.0),
+    (16384, 4096, 4096, 1200.0, 4190.0), (24576, 4096, 4096, 1790.0, 6240.0),
+    (49152, 4096, 4096, 3590.0, 12430.0), (65536, 4096, 4096, 4780.0, 16550.0),
+    (98304, 4096, 4096, 7170.0, 24810.0), (131072, 4096, 4096, 9560.0, 33050.0),
+    (258048, 4096, 4096, 18820.0, 65100.0), (299520, 4096, 4096, 21850.0, 75570.0),
+]
+
+
+def run_sweep(args):
+    """Every row of the page's shape table: operands randn (torch's seeded
+    generator on the device) quantized by the library's own 1 x 128 and
+    128 x 128 quantizers (not timed), then the GEMM timed with HIP events
+    around back-to-back launches, fp32 and bf16 output."""
+    torch, bsq = _gpu_setup()
+    dev = torch.device("cuda:0")
+    out_path = args.out
+    os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
+    open(out_path, "w").close()
+    gen = torch.Generator(device=dev)
+
+    def time_gemm(fn, n_iter):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(n_iter):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n_iter  # ms
+
+    for idx, (M, N, K, t_sol, t_prod) in enumerate(PAGE_SWEEP):
+        gen.manual_seed(1000 + idx)
+        a32 = torch.randn(M, K, device=dev, generator=gen)
+        b32 = torch.randn(N, K, device=dev, generator=gen)
+        aq = torch.empty(M, K, dtype=torch.uint8, device=dev)
+        bq = torch.empty(N, K, dtype=torch.uint8, device=dev)
+        sa = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+        sb = torch.empty(N // 128, K // 128, dtype=torch.float32, device=dev)
+        bsq.bsq_quant_fp8_rowblock(a32, aq, sa, 128)
+        bsq.bsq_quant_fp8_tile(b32, bq, sb, 128, 128)
+        del a32, b32
+        flops = 2.0 * M * N * K
+        n_it = max(3, min(50, int(2e13 / flops)))
+        row = {"row": idx, "m": M, "n": N, "k": K, "page_T_SOL_us": t_sol, "page_T_Prod_us": t_prod}
+        for name, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+            y = torch.empty(M, N, dtype=dt, device=dev)
+            ms = time_gemm(lambda: bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y), n_it)
+            tf = flops / (ms * 1e-3) / 1e12
+            row[f"us_{name}"] = round(ms * 1e3, 2)
+            row[f"TFLOP/s_{name}"] = round(tf, 1)
+            row[f"pct_peak_{name}"] = round(100 * tf / PEAK_FP8_TFLOPS, 1)
+            del y
+        _log("[sweep] " + json.dumps(row))
+        with open(out_path, "a") as f:
+            f.write(json.dumps(row) + "\n")
+        del aq, bq, sa, sb
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--suite", action="store_true")
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "suite.jsonl"))
+    ap.add_argument("--sweep", action="store_true",
+                    help="every row of the block_scaled_mm page's shape table (fp32 and bf16 output)")
+    ap.add_argument("--out", default=DEFAULT_SUITE_OUT)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy 512 MiB five times (counter calibration)")
@@ -414,6 +490,10 @@ def main():
         sys.exit(2)
     if args.suite:
         run_suite(args)
+    elif args.sweep:
+        if args.out == DEFAULT_SUITE_OUT:
+            args.out = os.path.join(ROOT, "gpurun_out", "sweep.jsonl")
+        run_sweep(args)
     else:
         run_main(args)
 

@@ -406,3 +406,48 @@ def test_half_tiles_mx(out):
     yr, T = OM.scaled_matmul(a, b, sa, sb, "e4m3", "e4m3", "e8m0")
     yh = host(y) if out == "f32" else OF.decode_bf16(host(y))
     assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
+
+
+# ------------------------------------ rows of the page's shape table -------
+
+@pytest.mark.parametrize("M,N,K", [(20480, 2048, 2048), (24576, 4096, 4096), (704512, 2048, 2048)])
+def test_page_sweep_rows_sampled(M, N, K):
+    """Rows of the block_scaled_mm page's shape table with the recipe's
+    operands (randn quantized on the GPU), fp32 and bf16 output, checked on
+    sampled rows.  An A of more than 65536 rows repeats one 65536-row randn
+    block (rows are independent in the quantizer and in the product), so
+    the oracle's rows come from that block; the largest row (704512 x 2048)
+    has more than 2^32 bytes of fp32 output."""
+    torch = _torch()
+    P = min(M, 65536)
+    say("page sweep row", M, N, K)
+    a_base = synth.randn_f32((P, K), 1100 + K)
+    b32 = synth.randn_f32((N, K), 1101 + K)
+    a_dev = to_dev(a_base)
+    if M > P:
+        a_dev = a_dev.repeat(M // P + 1, 1)[:M].contiguous()
+    aq = empty((M, K), torch.uint8)
+    bq = empty((N, K), torch.uint8)
+    sa = empty((M, K // 128), torch.float32)
+    sb = empty((N // 128, K // 128), torch.float32)
+    bsq.bsq_quant_fp8_rowblock(a_dev, aq, sa, 128)
+    bsq.bsq_quant_fp8_tile(to_dev(b32), bq, sb, 128, 128)
+    del a_dev
+    rows = _rows_sample(M, n=32, seed=M)
+    rt = torch.from_numpy(rows).to(aq.device)
+    ra, rsa = OQ.fp8_rowblock(a_base[rows % P])
+    rb, rsb = OQ.fp8_tile(b32)
+    assert_bytes_equal(host(aq.index_select(0, rt)), ra, "a codes (sampled rows)")
+    assert_bytes_equal(host(sa.index_select(0, rt)).view(np.uint32), rsa.view(np.uint32), "a scales")
+    assert_bytes_equal(host(bq), rb, "b codes")
+    yr, T = OM.blockwise_fp8(ra, rb, rsa, rsb)
+    for od in (torch.float32, torch.bfloat16):
+        y = filled((M, N), od, float("nan"))
+        bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y)
+        assert bool(torch.isfinite(y).all()), "unwritten output"
+        yh = host(y.index_select(0, rt))
+        if od == torch.bfloat16:
+            assert_within_T(OF.decode_bf16(yh), yr, T, "y rows (bf16)", bf16=True)
+        else:
+            assert_within_T(yh, yr, T, "y rows")
+        del y
