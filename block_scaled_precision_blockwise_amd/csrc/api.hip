@@ -183,6 +183,10 @@ bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8
 
 // --------------------------------------------------------------- matmuls --
 
+// Longest contraction the GEMM kernels address: their per-lane buffer
+// offsets reach 64 rows of K bytes in 32 bits.
+constexpr int64_t kMaxContraction = int64_t(1) << 24;
+
 bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t group_n,
                                     int64_t group_k, const uint8_t* a, const uint8_t* b,
                                     const float* a_scales, const float* b_scales, void* out,
@@ -197,7 +201,7 @@ bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t gro
   BSQ_CHECK(group_k == 128 && (group_n == 128 || group_n == 1), BSQ_ERR_UNSUPPORTED,
             "this build runs group_k 128 with group_n 1 or 128");
   BSQ_CHECK(N % 16 == 0, BSQ_ERR_UNSUPPORTED, "N must be a multiple of 16");
-  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30),
+  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
   if (M == 0 || N == 0) return ok();
   BSQ_CHECK_PTR(out);
@@ -235,7 +239,7 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
             "out_dtype must be F32 or BF16");
   BSQ_CHECK(K % 128 == 0 && N % 16 == 0, BSQ_ERR_UNSUPPORTED,
             "this build needs K % 128 == 0 and N % 16 == 0");
-  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30),
+  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
   GemmLaunch L{};
   if (scale_dtype == BSQ_E8M0) {
@@ -276,7 +280,7 @@ bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t*
                            const int8_t* w_qT, const float* x_s, const float* w_s, float* y,
                            int32_t* acc, void* stream) {
   BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
-  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30) && D_in <= (int64_t(1) << 30),
+  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30) && D_in <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
   if (B == 0 || D_out == 0) return ok();
   BSQ_CHECK_PTR(y);
@@ -365,7 +369,7 @@ bsq_status bsq_mxfp8_backward(int64_t M, int64_t N, int64_t K, const void* dY, c
             "out_dtype must be BF16 or F32");
   BSQ_CHECK(M % 128 == 0 && N % 128 == 0 && K % 128 == 0, BSQ_ERR_UNSUPPORTED,
             "M, N and K must be multiples of 128");
-  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= (int64_t(1) << 30),
+  BSQ_CHECK(M <= kMaxContraction && N <= kMaxContraction && K <= (int64_t(1) << 30),
             BSQ_ERR_UNSUPPORTED, "extent too large");
   const BwdLayout lay = bwd_layout(M, N, K);
   BSQ_CHECK(workspace_bytes >= lay.total, BSQ_ERR_SHAPE, "workspace too small");

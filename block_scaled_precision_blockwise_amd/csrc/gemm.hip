@@ -90,6 +90,14 @@ __device__ __forceinline__ void lds_dma4(i32x4 rsrc, int voff, uint32_t lds_addr
                : "memory", "m0");
 }
 
+// Buffer resource of `records` (>= 0, < 2^31) bytes from `base`.
+__device__ __forceinline__ i32x4 rsrc32(const uint8_t* base, int records) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane(int(uint32_t(b))),
+               __builtin_amdgcn_readfirstlane(int(uint32_t(b >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane(records), 0x00020000};
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
@@ -260,16 +268,24 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   const int lrow = 8 * w + (lane >> 3);
   const int llog = (lane & 7) ^ (lrow & 7);
   const int voff = lrow * K + 16 * llog;  // < 8 NW K
-  const int64_t a_bytes = int64_t(M) * K, b_bytes = int64_t(N) * K;
+  // bytes of each slice's rows that lie inside the operand, from the slice's
+  // first row (0 .. 64 rows of K bytes); at K-step ks a slice's descriptor
+  // starts ks * BK bytes into that row and covers the rest
+  int a_rec[SPW], b_rec[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    a_rec[s] = max(0, min(M - (m0 + 8 * NW * s), 8 * NW)) * K;
+    b_rec[s] = max(0, min(N - (n0 + 8 * NW * s), 8 * NW)) * K;
+  }
   const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_a + 8 * w * BK));
   const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_b + 8 * w * BK));
   auto gload_slice = [&](int ks, int st, int s) {
-    if (s < SPWA) {
-      const int64_t oa = int64_t(m0 + 8 * NW * s) * K + int64_t(ks) * BK;
-      lds_dma16(raw_rsrc(A + oa, a_bytes - oa), voff, la_base + uint32_t(st * TBM * BK + 8 * NW * s * BK));
-    }
-    const int64_t ob = int64_t(n0 + 8 * NW * s) * K + int64_t(ks) * BK;
-    lds_dma16(raw_rsrc(B + ob, b_bytes - ob), voff, lb_base + uint32_t(st * BN * BK + 8 * NW * s * BK));
+    const int kb = ks * BK;
+    if (s < SPWA)
+      lds_dma16(rsrc32(A + int64_t(m0 + 8 * NW * s) * K + kb, max(a_rec[s] - kb, 0)), voff,
+                la_base + uint32_t(st * TBM * BK + 8 * NW * s * BK));
+    lds_dma16(rsrc32(B + int64_t(n0 + 8 * NW * s) * K + kb, max(b_rec[s] - kb, 0)), voff,
+              lb_base + uint32_t(st * BN * BK + 8 * NW * s * BK));
   };
   auto gload = [&](int ks, int st) {
 #pragma unroll
@@ -338,15 +354,18 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   __syncthreads();
 
   // The next step's tiles stream into the idle stage while this one is
-  // multiplied.  The final step reloads its own tile into the idle stage so
-  // that the body has no branch.
+  // multiplied: each wave issues its A and B slice for it at the head of
+  // column blocks 0 .. SPW-1, between the MFMAs of the first half of the
+  // step (all at the head of the step stalls the MFMA issue behind the
+  // loads; spread over the whole step, the last ones land late).  The final
+  // step reloads its own tile into the idle stage so that the body has no
+  // branch.
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks & 1;
     const int kn = min(ks + 1, nk - 1);
     // the next group's scales during the last step of this group (the
     // buffer they go to was last read kSG steps ago)
     if (ks % kSG == kSG - 1 && ks + 1 < nk) sload((ks + 1) / kSG);
-    gload(kn, st ^ 1);
 
     const uint8_t* ta = lds_a + st * TBM * BK;
     const uint8_t* tb = lds_b + st * BN * BK;
@@ -405,6 +424,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     };
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
+      if (j < SPW) gload_slice(kn, st ^ 1, j);
       v8i pnext;
       if (j + PF < NB) pnext = bfrag(j + PF);
       const v8i pb = pq[0];

@@ -15,6 +15,9 @@
  *     enqueued and bsq_last_error() (thread-local) describes the cause.
  *   - A call with an empty extent (a zero size) is a valid no-op unless the
  *     call's own rules say otherwise.
+ *   - Matmul extents are at most 2^30, and a contraction length (K of a
+ *     matmul; M and N of the mxfp8 backward, whose two products contract
+ *     over them) at most 2^24; larger -> BSQ_ERR_UNSUPPORTED.
  *   - Non-finite inputs give unspecified results (the pages state all
  *     values are finite).
  *   - Format names: E4M3 = OCP float8_e4m3fn, E5M2 = OCP float8_e5m2,

@@ -134,3 +134,21 @@ def test_binding_refuses_cpu_tensors(L):
     x = torch.zeros(4, 128)
     with pytest.raises(ValueError):
         bsq.bsq_quant_fp8_rowblock(x, torch.zeros(4, 128, dtype=torch.uint8), torch.zeros(4, 1))
+
+
+def test_contraction_length_limit(L):
+    """Contraction lengths above 2^24 are refused before any device work:
+    the GEMM kernels address 64 rows of K bytes with 32-bit offsets."""
+    big = (1 << 24) + 128
+    _expect(L.bsq_blockwise_fp8_matmul(16, 256, big, 128, 128, A16, A16, A16, A16, A16,
+                                       bsq.BSQ_F32, None), UNSUP, L)
+    _expect(L.bsq_blockwise_fp8_matmul(16, 256, 1 << 24, 128, 128, A16, A16, A16, A16, A16,
+                                       bsq.BSQ_F32, None), DEVICE, L)
+    E4, E8, F32 = bsq.BSQ_E4M3, bsq.BSQ_E8M0, bsq.BSQ_F32
+    _expect(L.bsq_scaled_matmul(1, 8, 16, big, big // 32, big // 32, A16, E4, A16, E4, A16, A16,
+                                E8, A16, F32, None), UNSUP, L)
+    _expect(L.bsq_int8_matmul(2, big, 128, A16, A16, A16, A16, A16, None, None), UNSUP, L)
+    f = L.bsq_mxfp8_backward
+    E5, BF = bsq.BSQ_E5M2, bsq.BSQ_BF16
+    for M, N in ((big, 256), (256, big)):
+        _expect(f(M, N, 256, A16, A16, A16, E5, BF, A16, A16, A16, 1 << 62, None), UNSUP, L)
