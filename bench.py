@@ -139,6 +139,15 @@ class KernelTimer:
         return total / max(n, 1)
 
 
+def _queue_ahead(torch):
+    """Occupy the stream with torch's spin kernel (a few milliseconds) so
+    that the host has queued every launch of a timed batch before the GPU
+    reaches the batch: the events then see the kernels back to back, not
+    the host's per-call cost (about 8 us per binding call, more than a
+    short quantizer takes)."""
+    torch.cuda._sleep(10_000_000)
+
+
 # --------------------------------------------------------------- main ----
 
 def run_main(args):
@@ -298,6 +307,7 @@ def run_suite(args):
         torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
+        _queue_ahead(torch)
         s.record()
         for i in range(n_iter):
             fn(i % rotate)
@@ -435,6 +445,7 @@ def run_sweep(args):
         torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
+        _queue_ahead(torch)
         s.record()
         for _ in range(n_iter):
             fn()
