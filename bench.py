@@ -401,6 +401,16 @@ def run_suite(args):
     ms = time_launches(lambda i: bsq.bsq_mxfp8_backward(dY, W, X, dX, dW, wsb), 10)
     mfma_row("mxfp8_backward (4 quant + 2 GEMM)", f"dY {M}x{N}, W {N}x{K}, X {M}x{K} e5m2 bf16 out", ms,
              2 * 2 * M * N * K, PEAK_FP8_TFLOPS)
+    # the same backward with its four operands already quantized (the page's
+    # pre-computed scales): only the two products
+    shp = bsq.mxfp8_backward_operand_shapes(M, N, K)
+    ops = {n: (torch.empty(c, dtype=torch.uint8, device=dev), torch.empty(sc, dtype=torch.uint8, device=dev))
+           for n, (c, sc) in shp.items()}
+    bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dY, W=W, X=X, **ops)
+    ms = time_launches(lambda i: bsq.bsq_mxfp8_backward_gemms(M, N, K, dX=dX, dW=dW, **ops), 10)
+    mfma_row("mxfp8_backward, pre-quantized (2 GEMM)", f"dY {M}x{N}, W {N}x{K}, X {M}x{K} e5m2 bf16 out", ms,
+             2 * 2 * M * N * K, PEAK_FP8_TFLOPS)
+    del ops
     codes = torch.empty(N, M, dtype=torch.uint8, device=dev)
     scs = torch.empty(N, M // 32, dtype=torch.uint8, device=dev)
     ms = time_launches(lambda i: bsq.bsq_quant_mx(dY, codes, scs, axis=0, code_dtype=bsq.BSQ_E5M2), 20)

@@ -31,6 +31,7 @@ __all__ = [
     "bsq_blockwise_fp8_matmul", "bsq_scaled_matmul", "bsq_int8_matmul",
     "bsq_int8_workspace_bytes", "bsq_int8_per_channel_matmul",
     "bsq_mxfp8_backward_workspace_bytes", "bsq_mxfp8_backward",
+    "mxfp8_backward_operand_shapes", "bsq_mxfp8_backward_quantize", "bsq_mxfp8_backward_gemms",
     "BsqError",
 ]
 
@@ -63,6 +64,10 @@ _SIGNATURES = {
     "bsq_int8_per_channel_matmul": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "bsq_mxfp8_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "bsq_mxfp8_backward": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _INT, _P, _P, _P, _SZ, _P]),
+    "bsq_mxfp8_backward_quantize": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P]),
+    "bsq_mxfp8_backward_gemms": (_INT, [_I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P]),
 }
 
 
@@ -368,3 +373,70 @@ def bsq_mxfp8_backward(dY, W, X, dX, dW, workspace, code_dtype: int = BSQ_E5M2, 
     _raise(lib().bsq_mxfp8_backward(M, N, K, _ptr(dY), _ptr(W), _ptr(X), code_dtype, od, _ptr(dX),
                                     _ptr(dW), _ptr(workspace), nbytes, _stream(stream)),
            "bsq_mxfp8_backward")
+
+
+def mxfp8_backward_operand_shapes(M: int, N: int, K: int) -> dict:
+    """(codes shape, scales shape) of the four MX operands of the backward:
+    dyn (dY blocked along N), wt (W blocked along N, transposed), dyt (dY
+    blocked along M, transposed), xt (X blocked along M, transposed)."""
+    return {"dyn": ((M, N), (M, N // 32)), "wt": ((K, N), (K, N // 32)),
+            "dyt": ((N, M), (N, M // 32)), "xt": ((K, M), (K, M // 32))}
+
+
+def _pair(p, name, shapes):
+    if p is None:
+        return None, None
+    c, sc = p
+    _dev(c, sc)
+    _expect(c, c.dtype, shapes[name][0], name + " codes")
+    _expect(sc, sc.dtype, shapes[name][1], name + " scales")
+    _bytes1(c, name + " codes")
+    _bytes1(sc, name + " scales")
+    return _ptr(c), _ptr(sc)
+
+
+def bsq_mxfp8_backward_quantize(M: int, N: int, K: int, dY=None, W=None, X=None, dyn=None, wt=None,
+                                dyt=None, xt=None, code_dtype: int = BSQ_E5M2, stream=None):
+    """Quantize bf16 dY [M, N], W [N, K], X [M, K] into the requested MX
+    operands; each of dyn, wt, dyt, xt is None or a (codes, scales) pair of
+    one-byte tensors shaped as mxfp8_backward_operand_shapes gives."""
+    torch = _torch()
+    shapes = mxfp8_backward_operand_shapes(M, N, K)
+    _dev(dY, W, X)
+    if dY is not None:
+        _expect(dY, torch.bfloat16, (M, N), "dY")
+    if W is not None:
+        _expect(W, torch.bfloat16, (N, K), "W")
+    if X is not None:
+        _expect(X, torch.bfloat16, (M, K), "X")
+    ptrs = [_pair(p, n, shapes) for n, p in (("dyn", dyn), ("wt", wt), ("dyt", dyt), ("xt", xt))]
+    flat = [v for pr in ptrs for v in pr]
+    _raise(lib().bsq_mxfp8_backward_quantize(M, N, K, _ptr(dY), _ptr(W), _ptr(X), code_dtype, *flat,
+                                             _stream(stream)), "bsq_mxfp8_backward_quantize")
+
+
+def bsq_mxfp8_backward_gemms(M: int, N: int, K: int, dyn=None, wt=None, dyt=None, xt=None, dX=None, dW=None,
+                             code_dtype: int = BSQ_E5M2, stream=None):
+    """dX [M, K] = dyn . wt and/or dW [N, K] = dyt . xt from pre-quantized
+    MX operands ((codes, scales) pairs as mxfp8_backward_operand_shapes
+    gives); outputs float32 or bfloat16 (one dtype for both)."""
+    torch = _torch()
+    shapes = mxfp8_backward_operand_shapes(M, N, K)
+    _dev(dX, dW)
+    outs = [t for t in (dX, dW) if t is not None]
+    od = BSQ_F32
+    if outs:
+        dts = {t.dtype for t in outs}
+        if len(dts) != 1:
+            raise ValueError("dX and dW must have one dtype")
+        od = {torch.float32: BSQ_F32, torch.bfloat16: BSQ_BF16}.get(outs[0].dtype)
+        if od is None:
+            raise TypeError("outputs must be float32 or bfloat16")
+    if dX is not None and tuple(dX.shape) != (M, K):
+        raise ValueError(f"dX must have shape {(M, K)}")
+    if dW is not None and tuple(dW.shape) != (N, K):
+        raise ValueError(f"dW must have shape {(N, K)}")
+    ptrs = [_pair(p, n, shapes) for n, p in (("dyn", dyn), ("wt", wt), ("dyt", dyt), ("xt", xt))]
+    flat = [v for pr in ptrs for v in pr]
+    _raise(lib().bsq_mxfp8_backward_gemms(M, N, K, code_dtype, od, *flat, _ptr(dX), _ptr(dW), _stream(stream)),
+           "bsq_mxfp8_backward_gemms")

@@ -333,6 +333,67 @@ struct BwdLayout {
       total;
 };
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+// The four MX operands of the two backward products, each K-contiguous
+// (blocks of 32 along the product's contraction axis):
+//   dyn: dY blocked along N [M, N] (+ [M, N/32] scales)      A of dX
+//   wt:  W blocked along N, transposed [K, N] (+ [K, N/32])   B of dX
+//   dyt: dY blocked along M, transposed [N, M] (+ [N, M/32])  A of dW
+//   xt:  X blocked along M, transposed [K, M] (+ [K, M/32])   B of dW
+struct BwdOps {
+  const uint8_t *dyn_c, *dyn_s, *wt_c, *wt_s, *dyt_c, *dyt_s, *xt_c, *xt_s;
+};
+
+bsq_status bwd_check_dims(int64_t M, int64_t N, int64_t K, int code_dtype) {
+  BSQ_CHECK(M >= 0 && N >= 0 && K >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(known_dtype(code_dtype), BSQ_ERR_DTYPE, "unknown dtype");
+  BSQ_CHECK(is_fp8(code_dtype), BSQ_ERR_UNSUPPORTED, "code_dtype must be E4M3 or E5M2");
+  BSQ_CHECK(M % 128 == 0 && N % 128 == 0 && K % 128 == 0, BSQ_ERR_UNSUPPORTED,
+            "M, N and K must be multiples of 128");
+  BSQ_CHECK(M <= kMaxContraction && N <= kMaxContraction && K <= (int64_t(1) << 30),
+            BSQ_ERR_UNSUPPORTED, "extent too large");
+  return BSQ_OK;
+}
+
+// Quantizes the bf16 sources into whichever operands have codes != NULL.
+bsq_status bwd_quantize(int64_t M, int64_t N, int64_t K, const void* dY, const void* W, const void* X,
+                        bool e5, uint8_t* dyn_c, uint8_t* dyn_s, uint8_t* wt_c, uint8_t* wt_s,
+                        uint8_t* dyt_c, uint8_t* dyt_s, uint8_t* xt_c, uint8_t* xt_s, hipStream_t st) {
+  bsq_status s = BSQ_OK;
+  if (dyn_c != nullptr && (s = launch_mx(M, N, 1, dY, true, dyn_c, e5, dyn_s, st)) != BSQ_OK) return s;
+  if (wt_c != nullptr && (s = launch_mx(N, K, 0, W, true, wt_c, e5, wt_s, st)) != BSQ_OK) return s;
+  if (dyt_c != nullptr && (s = launch_mx(M, N, 0, dY, true, dyt_c, e5, dyt_s, st)) != BSQ_OK) return s;
+  if (xt_c != nullptr && (s = launch_mx(M, K, 0, X, true, xt_c, e5, xt_s, st)) != BSQ_OK) return s;
+  return ok();
+}
+
+// dX = dyn . wt (contract N) if dX != NULL; dW = dyt . xt (contract M) if
+// dW != NULL.  An empty contraction writes zeros.
+bsq_status bwd_gemms(int64_t M, int64_t N, int64_t K, bool e5, bool out_bf16, const BwdOps& o, void* dX,
+                     void* dW, hipStream_t st) {
+  GemmLaunch L{};
+  L.mode = MODE_MX;
+  L.batch = 1;
+  L.out_bf16 = out_bf16;
+  L.fa_e5m2 = L.fb_e5m2 = e5;
+  if (dX != nullptr && M > 0 && K > 0) {
+    L.M = M; L.N = K; L.K = N;
+    L.A = o.dyn_c; L.SA = o.dyn_s;
+    L.B = o.wt_c; L.SB = o.wt_s;
+    L.out = dX;
+    const bsq_status s = launch_gemm(L, st);
+    if (s != BSQ_OK) return s;
+  }
+  if (dW != nullptr && N > 0 && K > 0) {
+    L.M = N; L.N = K; L.K = M;
+    L.A = o.dyt_c; L.SA = o.dyt_s;
+    L.B = o.xt_c; L.SB = o.xt_s;
+    L.out = dW;
+    const bsq_status s = launch_gemm(L, st);
+    if (s != BSQ_OK) return s;
+  }
+  return ok();
+}
+
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
   BwdLayout L{};
   size_t o = 0;
@@ -362,15 +423,11 @@ size_t bsq_mxfp8_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 bsq_status bsq_mxfp8_backward(int64_t M, int64_t N, int64_t K, const void* dY, const void* W,
                               const void* X, int code_dtype, int out_dtype, void* dX, void* dW,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  BSQ_CHECK(M >= 0 && N >= 0 && K >= 0, BSQ_ERR_SHAPE, "negative size");
-  BSQ_CHECK(known_dtype(code_dtype) && known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown dtype");
-  BSQ_CHECK(is_fp8(code_dtype), BSQ_ERR_UNSUPPORTED, "code_dtype must be E4M3 or E5M2");
+  bsq_status s = bwd_check_dims(M, N, K, code_dtype);
+  if (s != BSQ_OK) return s;
+  BSQ_CHECK(known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown dtype");
   BSQ_CHECK(out_dtype == BSQ_BF16 || out_dtype == BSQ_F32, BSQ_ERR_UNSUPPORTED,
             "out_dtype must be BF16 or F32");
-  BSQ_CHECK(M % 128 == 0 && N % 128 == 0 && K % 128 == 0, BSQ_ERR_UNSUPPORTED,
-            "M, N and K must be multiples of 128");
-  BSQ_CHECK(M <= kMaxContraction && N <= kMaxContraction && K <= (int64_t(1) << 30),
-            BSQ_ERR_UNSUPPORTED, "extent too large");
   const BwdLayout lay = bwd_layout(M, N, K);
   BSQ_CHECK(workspace_bytes >= lay.total, BSQ_ERR_SHAPE, "workspace too small");
   if (K == 0 || (M == 0 && N == 0)) return ok();  // both outputs are empty
@@ -386,33 +443,95 @@ bsq_status bsq_mxfp8_backward(int64_t M, int64_t N, int64_t K, const void* dY, c
   hipStream_t st = as_stream(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const bool e5 = code_dtype == BSQ_E5M2;
-  bsq_status s;
-  s = launch_mx(M, N, 1, dY, true, ws + lay.dyn_codes, e5, ws + lay.dyn_scales, st);
+  if (M > 0 && N > 0) {
+    s = bwd_quantize(M, N, K, dY, W, X, e5, ws + lay.dyn_codes, ws + lay.dyn_scales, ws + lay.wt_codes,
+                     ws + lay.wt_scales, ws + lay.dyt_codes, ws + lay.dyt_scales, ws + lay.xt_codes,
+                     ws + lay.xt_scales, st);
+    if (s != BSQ_OK) return s;
+  }
+  const BwdOps o{ws + lay.dyn_codes, ws + lay.dyn_scales, ws + lay.wt_codes, ws + lay.wt_scales,
+                 ws + lay.dyt_codes, ws + lay.dyt_scales, ws + lay.xt_codes, ws + lay.xt_scales};
+  return bwd_gemms(M, N, K, e5, out_dtype == BSQ_BF16, o, M > 0 ? dX : nullptr, N > 0 ? dW : nullptr, st);
+}
+
+bsq_status bsq_mxfp8_backward_quantize(int64_t M, int64_t N, int64_t K, const void* dY, const void* W,
+                                       const void* X, int code_dtype, uint8_t* dyn_codes,
+                                       uint8_t* dyn_scales, uint8_t* wt_codes, uint8_t* wt_scales,
+                                       uint8_t* dyt_codes, uint8_t* dyt_scales, uint8_t* xt_codes,
+                                       uint8_t* xt_scales, void* stream) {
+  bsq_status s = bwd_check_dims(M, N, K, code_dtype);
   if (s != BSQ_OK) return s;
-  s = launch_mx(N, K, 0, W, true, ws + lay.wt_codes, e5, ws + lay.wt_scales, st);
+  // an operand is produced iff its codes pointer is given; it then needs its
+  // scales and its source (unless it is empty)
+  struct Req {
+    uint8_t* c;
+    uint8_t* sc;
+    const void* src;
+    int64_t r, cl;
+    const char* what;
+  };
+  const Req req[4] = {{dyn_codes, dyn_scales, dY, M, N, "dY blocked along N"},
+                      {wt_codes, wt_scales, W, N, K, "W blocked along N"},
+                      {dyt_codes, dyt_scales, dY, M, N, "dY blocked along M"},
+                      {xt_codes, xt_scales, X, M, K, "X blocked along M"}};
+  bool live[4] = {false, false, false, false};
+  for (int i = 0; i < 4; ++i) {
+    const Req& q = req[i];
+    if (q.c == nullptr) {
+      BSQ_CHECK(q.sc == nullptr, BSQ_ERR_NULL, std::string(q.what) + ": scales given without codes");
+      continue;
+    }
+    if (q.r == 0 || q.cl == 0) continue;
+    BSQ_CHECK(q.sc != nullptr, BSQ_ERR_NULL, std::string(q.what) + ": scales are NULL");
+    BSQ_CHECK(aligned16(q.c) && aligned16(q.sc), BSQ_ERR_ALIGN,
+              std::string(q.what) + ": codes or scales not 16-byte aligned");
+    BSQ_CHECK(q.src != nullptr, BSQ_ERR_NULL, std::string(q.what) + ": source is NULL");
+    BSQ_CHECK(aligned16(q.src), BSQ_ERR_ALIGN, std::string(q.what) + ": source not 16-byte aligned");
+    live[i] = true;
+  }
+  if (!(live[0] || live[1] || live[2] || live[3])) return ok();
+  BSQ_DEVICE();
+  return bwd_quantize(M, N, K, dY, W, X, code_dtype == BSQ_E5M2, live[0] ? dyn_codes : nullptr, dyn_scales,
+                      live[1] ? wt_codes : nullptr, wt_scales, live[2] ? dyt_codes : nullptr, dyt_scales,
+                      live[3] ? xt_codes : nullptr, xt_scales, as_stream(stream));
+}
+
+bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dtype, int out_dtype,
+                                    const uint8_t* dyn_codes, const uint8_t* dyn_scales,
+                                    const uint8_t* wt_codes, const uint8_t* wt_scales,
+                                    const uint8_t* dyt_codes, const uint8_t* dyt_scales,
+                                    const uint8_t* xt_codes, const uint8_t* xt_scales, void* dX, void* dW,
+                                    void* stream) {
+  bsq_status s = bwd_check_dims(M, N, K, code_dtype);
   if (s != BSQ_OK) return s;
-  s = launch_mx(M, N, 0, dY, true, ws + lay.dyt_codes, e5, ws + lay.dyt_scales, st);
-  if (s != BSQ_OK) return s;
-  s = launch_mx(M, K, 0, X, true, ws + lay.xt_codes, e5, ws + lay.xt_scales, st);
-  if (s != BSQ_OK) return s;
-  GemmLaunch L{};
-  L.mode = MODE_MX;
-  L.batch = 1;
-  L.out_bf16 = out_dtype == BSQ_BF16;
-  L.fa_e5m2 = L.fb_e5m2 = e5;
-  // dX [M, K] = dY [M, N] . W^T-layout [K, N] (contract N)
-  L.M = M; L.N = K; L.K = N;
-  L.A = ws + lay.dyn_codes; L.SA = ws + lay.dyn_scales;
-  L.B = ws + lay.wt_codes; L.SB = ws + lay.wt_scales;
-  L.out = dX;
-  s = launch_gemm(L, st);
-  if (s != BSQ_OK) return s;
-  // dW [N, K] = dY^T-layout [N, M] . X^T-layout [K, M] (contract M)
-  L.M = N; L.N = K; L.K = M;
-  L.A = ws + lay.dyt_codes; L.SA = ws + lay.dyt_scales;
-  L.B = ws + lay.xt_codes; L.SB = ws + lay.xt_scales;
-  L.out = dW;
-  return launch_gemm(L, st);
+  BSQ_CHECK(known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown dtype");
+  BSQ_CHECK(out_dtype == BSQ_BF16 || out_dtype == BSQ_F32, BSQ_ERR_UNSUPPORTED,
+            "out_dtype must be BF16 or F32");
+  const bool want_dx = dX != nullptr && M > 0 && K > 0;
+  const bool want_dw = dW != nullptr && N > 0 && K > 0;
+  if (want_dx) {
+    BSQ_CHECK(aligned16(dX), BSQ_ERR_ALIGN, "dX is not 16-byte aligned");
+    if (N > 0) {
+      BSQ_CHECK_PTR(dyn_codes);
+      BSQ_CHECK_PTR(dyn_scales);
+      BSQ_CHECK_PTR(wt_codes);
+      BSQ_CHECK_PTR(wt_scales);
+    }
+  }
+  if (want_dw) {
+    BSQ_CHECK(aligned16(dW), BSQ_ERR_ALIGN, "dW is not 16-byte aligned");
+    if (M > 0) {
+      BSQ_CHECK_PTR(dyt_codes);
+      BSQ_CHECK_PTR(dyt_scales);
+      BSQ_CHECK_PTR(xt_codes);
+      BSQ_CHECK_PTR(xt_scales);
+    }
+  }
+  if (!want_dx && !want_dw) return ok();
+  BSQ_DEVICE();
+  const BwdOps o{dyn_codes, dyn_scales, wt_codes, wt_scales, dyt_codes, dyt_scales, xt_codes, xt_scales};
+  return bwd_gemms(M, N, K, code_dtype == BSQ_E5M2, out_dtype == BSQ_BF16, o, want_dx ? dX : nullptr,
+                   want_dw ? dW : nullptr, as_stream(stream));
 }
 
 }  // extern "C"

@@ -206,6 +206,50 @@ bsq_status bsq_mxfp8_backward(int64_t M, int64_t N, int64_t K, const void* dY, c
                               const void* X, int code_dtype, int out_dtype, void* dX, void* dW,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same backward in two calls, for pre-quantized operands and for
+ * quantizing an operand once and reusing it (mxfp8 backward, parameters:
+ * the optional pre-computed scales of output_grad, weights and
+ * input_activation; packed scales for pre-quantized inputs; spilling the
+ * quantized blocks to HBM and reloading them).  The four operands of the
+ * two products, each a codes array plus an E8M0 scale array (one byte per
+ * 32-element block, rows of blocks contiguous: four scales to a 32-bit
+ * word), all row-major and K-contiguous along the product's contraction:
+ *   dyn: dY blocked along N,  codes [M, N], scales [M, N/32]   (A of dX)
+ *   wt:  W blocked along N, transposed,  codes [K, N], scales [K, N/32]
+ *        (B of dX)
+ *   dyt: dY blocked along M, transposed, codes [N, M], scales [N, M/32]
+ *        (A of dW)
+ *   xt:  X blocked along M, transposed,  codes [K, M], scales [K, M/32]
+ *        (B of dW)
+ * bsq_mxfp8_backward computes exactly these four (into its workspace) and
+ * then exactly these two products, so the two-call path gives the same
+ * bits.
+ *
+ * bsq_mxfp8_backward_quantize: bf16 dY [M, N], W [N, K], X [M, K] ->
+ * each operand whose codes pointer is non-NULL (its scales then must be
+ * non-NULL too, and its source).  E.g. W's operand once per weight update,
+ * dY's two per micro-batch.  A NULL codes pointer with non-NULL scales ->
+ * BSQ_ERR_NULL.
+ *
+ * bsq_mxfp8_backward_gemms: dX [M, K] = dyn . wt (contract N) when dX is
+ * non-NULL, dW [N, K] = dyt . xt (contract M) when dW is non-NULL; the
+ * operands of a requested product must be non-NULL.  out_dtype BSQ_BF16 or
+ * BSQ_F32 for both.  An empty contraction (N = 0 for dX, M = 0 for dW)
+ * writes zeros.
+ * Rules for both: M, N, K multiples of 128 (else UNSUPPORTED; negative ->
+ * SHAPE); code_dtype BSQ_E5M2 or BSQ_E4M3 for every operand. */
+bsq_status bsq_mxfp8_backward_quantize(int64_t M, int64_t N, int64_t K, const void* dY, const void* W,
+                                       const void* X, int code_dtype, uint8_t* dyn_codes,
+                                       uint8_t* dyn_scales, uint8_t* wt_codes, uint8_t* wt_scales,
+                                       uint8_t* dyt_codes, uint8_t* dyt_scales, uint8_t* xt_codes,
+                                       uint8_t* xt_scales, void* stream);
+bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dtype, int out_dtype,
+                                    const uint8_t* dyn_codes, const uint8_t* dyn_scales,
+                                    const uint8_t* wt_codes, const uint8_t* wt_scales,
+                                    const uint8_t* dyt_codes, const uint8_t* dyt_scales,
+                                    const uint8_t* xt_codes, const uint8_t* xt_scales, void* dX, void* dW,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,11 @@ operands are blocked along its own contraction axis:
         X blocked along M (laid out transposed [K, M]).
 Each product is then scaled_matmul with both operands K-contiguous.
 
+Pre-quantized operands (the page's optional pre-computed scales for
+output_grad, weights and input_activation, with packed scales): reading -
+the caller then supplies the four operands above already quantized, in the
+same layouts, and only the two products remain (``backward_products``).
+
 Pinned (tests/test_oracle_backward.py) by inputs that quantize losslessly,
 for which both products must equal the plain float64 products of the bf16
 inputs, and by the transposition structure (swapping operands or axes
@@ -48,6 +53,12 @@ def mxfp8_backward(dY_bits, W_bits, X_bits, fmt=F.E5M2, with_bound=True):
     """Returns (dX float64 [M, K], T_dX, dW float64 [N, K], T_dW, ops) where
     ops are the quantized operands from ``quantize_operands``."""
     ops = quantize_operands(dY_bits, W_bits, X_bits, fmt)
+    return backward_products(ops, fmt, with_bound) + (ops,)
+
+
+def backward_products(ops, fmt=F.E5M2, with_bound=True):
+    """The two products of already quantized operands (a dict as
+    ``quantize_operands`` returns): (dX, T_dX, dW, T_dW), float64."""
     a, sa = ops["dY_n"]
     b, sb = ops["W_t"]
     dX, T_dX = scaled_matmul(a[None], b[None], sa[None], sb[None], fmt, fmt,
@@ -56,4 +67,4 @@ def mxfp8_backward(dY_bits, W_bits, X_bits, fmt=F.E5M2, with_bound=True):
     b, sb = ops["X_t"]
     dW, T_dW = scaled_matmul(a[None], b[None], sa[None], sb[None], fmt, fmt,
                              "e8m0", with_bound=with_bound)
-    return dX[0], (T_dX[0] if with_bound else None), dW[0], (T_dW[0] if with_bound else None), ops
+    return dX[0], (T_dX[0] if with_bound else None), dW[0], (T_dW[0] if with_bound else None)

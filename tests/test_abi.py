@@ -152,3 +152,32 @@ def test_contraction_length_limit(L):
     E5, BF = bsq.BSQ_E5M2, bsq.BSQ_BF16
     for M, N in ((big, 256), (256, big)):
         _expect(f(M, N, 256, A16, A16, A16, E5, BF, A16, A16, A16, 1 << 62, None), UNSUP, L)
+
+
+def test_backward_split_validation(L):
+    """The two-call backward: an operand is produced iff its codes pointer
+    is given; a product is computed iff its output pointer is given."""
+    q, g = L.bsq_mxfp8_backward_quantize, L.bsq_mxfp8_backward_gemms
+    E5, BF, F32 = bsq.BSQ_E5M2, bsq.BSQ_BF16, bsq.BSQ_F32
+    ops = [A16] * 8
+    # nothing requested: a no-op, no device needed
+    _expect(q(256, 256, 256, None, None, None, E5, *([None] * 8), None), OK, L)
+    _expect(g(256, 256, 256, E5, BF, *([None] * 8), None, None, None), OK, L)
+    # shape and dtype rules of the one-call backward
+    _expect(q(256, 256, 200, A16, A16, A16, E5, *ops, None), UNSUP, L)
+    _expect(q(-128, 256, 256, A16, A16, A16, E5, *ops, None), SHAPE, L)
+    _expect(q(256, 256, 256, A16, A16, A16, bsq.BSQ_I8, *ops, None), UNSUP, L)
+    _expect(g(256, 256, 256, E5, bsq.BSQ_I8, *ops, A16, A16, None), UNSUP, L)
+    # scales without codes, codes without scales, a missing source
+    _expect(q(256, 256, 256, A16, A16, A16, E5, None, A16, *([None] * 6), None), NULL, L)
+    _expect(q(256, 256, 256, A16, A16, A16, E5, A16, None, *([None] * 6), None), NULL, L)
+    _expect(q(256, 256, 256, None, A16, A16, E5, A16, A16, *([None] * 6), None), NULL, L)
+    _expect(q(256, 256, 256, A16, A16, A16, E5, A4, A16, *([None] * 6), None), ALIGN, L)
+    # W's operand alone needs only W
+    _expect(q(256, 256, 256, None, A16, None, E5, None, None, A16, A16, *([None] * 4), None), DEVICE, L)
+    # a requested product needs its two operands, not the other product's
+    _expect(g(256, 256, 256, E5, BF, None, A16, A16, A16, *([None] * 4), A16, None, None), NULL, L)
+    _expect(g(256, 256, 256, E5, BF, A16, A16, A16, A16, *([None] * 4), A16, None, None), DEVICE, L)
+    _expect(g(256, 256, 256, E5, F32, *([None] * 4), A16, A16, A16, A16, None, A4, None), ALIGN, L)
+    # an empty contraction needs no operands (the output is zeros)
+    _expect(g(256, 0, 256, E5, BF, *([None] * 8), A16, None, None), DEVICE, L)

@@ -377,6 +377,101 @@ def test_backward_full_size_sampled():
     assert np.all(np.isfinite(dXh)) and np.all(np.isfinite(dWh))
 
 
+# ----------------------------------------- backward in two calls (NEXT) ---
+# Pre-quantized operands, provided scales and quantize-once reuse (mxfp8
+# backward: the optional pre-computed scales, packed scales, quantized
+# blocks spilled to HBM and reloaded).
+
+def _operand_tensors(M, N, K):
+    torch = _torch()
+    shapes = bsq.mxfp8_backward_operand_shapes(M, N, K)
+    return {n: (empty(c, torch.uint8), empty(sc, torch.uint8)) for n, (c, sc) in shapes.items()}
+
+
+def _two_call(dYd, Wd, Xd, M, N, K, out_dtype, code, ops=None):
+    ops = ops or _operand_tensors(M, N, K)
+    bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dYd, W=Wd, X=Xd, dyn=ops["dyn"], wt=ops["wt"],
+                                    dyt=ops["dyt"], xt=ops["xt"], code_dtype=code)
+    dX = filled((M, K), out_dtype, float("nan"))
+    dW = filled((N, K), out_dtype, float("nan"))
+    bsq.bsq_mxfp8_backward_gemms(M, N, K, dyn=ops["dyn"], wt=ops["wt"], dyt=ops["dyt"], xt=ops["xt"],
+                                 dX=dX, dW=dW, code_dtype=code)
+    return dX, dW, ops
+
+
+@pytest.mark.parametrize("fmt", ["e5m2", "e4m3"])
+def test_backward_two_calls_equal_one_call(fmt):
+    """quantize + gemms gives the one-call backward's bits; the quantized
+    operands equal the oracle's codes and scales byte for byte."""
+    torch = _torch()
+    M, N, K = 384, 256, 640
+    say("backward two calls", fmt, M, N, K)
+    code = bsq.BSQ_E5M2 if fmt == "e5m2" else bsq.BSQ_E4M3
+    dYb = synth.randn_bf16_bits((M, N), 50)
+    Wb = synth.randn_bf16_bits((N, K), 51)
+    Xb = synth.randn_bf16_bits((M, K), 52)
+    dX1, dW1 = _run_backward(dYb, Wb, Xb, torch.float32, code)
+    dYd, Wd, Xd = (to_dev(v).view(torch.bfloat16) for v in (dYb, Wb, Xb))
+    dX2, dW2, ops = _two_call(dYd, Wd, Xd, M, N, K, torch.float32, code)
+    assert_bytes_equal(host(dX2).view(np.uint32), host(dX1).view(np.uint32), "dX")
+    assert_bytes_equal(host(dW2).view(np.uint32), host(dW1).view(np.uint32), "dW")
+    ref = OB.quantize_operands(dYb, Wb, Xb, fmt)
+    for ours, theirs in (("dyn", "dY_n"), ("wt", "W_t"), ("dyt", "dY_t"), ("xt", "X_t")):
+        assert_bytes_equal(host(ops[ours][0]), ref[theirs][0], ours + " codes")
+        assert_bytes_equal(host(ops[ours][1]), ref[theirs][1], ours + " scales")
+    dX, T_dX, dW, T_dW = OB.backward_products(ref, fmt)
+    assert_within_T(host(dX2), dX, T_dX, "dX")
+    assert_within_T(host(dW2), dW, T_dW, "dW")
+
+
+def test_backward_prequantized_operands_from_the_oracle():
+    """Operands quantized by the oracle on the host and handed over with
+    their scales: only the two products run on the GPU."""
+    torch = _torch()
+    M, N, K = 256, 384, 512
+    say("backward pre-quantized", M, N, K)
+    dYb = synth.randn_bf16_bits((M, N), 53)
+    Wb = synth.randn_bf16_bits((N, K), 54)
+    Xb = synth.randn_bf16_bits((M, K), 55)
+    ref = OB.quantize_operands(dYb, Wb, Xb, "e5m2")
+    ops = {ours: (to_dev(ref[theirs][0]), to_dev(ref[theirs][1]))
+           for ours, theirs in (("dyn", "dY_n"), ("wt", "W_t"), ("dyt", "dY_t"), ("xt", "X_t"))}
+    dX = filled((M, K), torch.bfloat16, float("nan"))
+    dW = filled((N, K), torch.bfloat16, float("nan"))
+    bsq.bsq_mxfp8_backward_gemms(M, N, K, dX=dX, dW=dW, code_dtype=bsq.BSQ_E5M2, **ops)
+    rX, T_dX, rW, T_dW = OB.backward_products(ref, "e5m2")
+    assert_within_T(OF.decode_bf16(host(dX)), rX, T_dX, "dX", bf16=True)
+    assert_within_T(OF.decode_bf16(host(dW)), rW, T_dW, "dW", bf16=True)
+
+
+def test_backward_weight_operand_quantized_once():
+    """W's operand is quantized once and reused for two micro-batches; each
+    micro-batch's outputs equal the one-call backward's bits, and so does a
+    call that asks for dX alone."""
+    torch = _torch()
+    M, N, K = 256, 256, 384
+    say("backward reuse W", M, N, K)
+    Wb = synth.randn_bf16_bits((N, K), 56)
+    Wd = to_dev(Wb).view(torch.bfloat16)
+    ops = _operand_tensors(M, N, K)
+    bsq.bsq_mxfp8_backward_quantize(M, N, K, W=Wd, wt=ops["wt"])
+    for mb in range(2):
+        dYb = synth.randn_bf16_bits((M, N), 60 + 2 * mb)
+        Xb = synth.randn_bf16_bits((M, K), 61 + 2 * mb)
+        dYd, Xd = to_dev(dYb).view(torch.bfloat16), to_dev(Xb).view(torch.bfloat16)
+        bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dYd, X=Xd, dyn=ops["dyn"], dyt=ops["dyt"], xt=ops["xt"])
+        dX = filled((M, K), torch.bfloat16, float("nan"))
+        dW = filled((N, K), torch.bfloat16, float("nan"))
+        bsq.bsq_mxfp8_backward_gemms(M, N, K, dX=dX, dW=dW, **ops)
+        dX1, dW1 = _run_backward(dYb, Wb, Xb, torch.bfloat16, bsq.BSQ_E5M2)
+        assert_bytes_equal(host(dX).view(np.uint16), host(dX1).view(np.uint16), f"dX mb {mb}")
+        assert_bytes_equal(host(dW).view(np.uint16), host(dW1).view(np.uint16), f"dW mb {mb}")
+    # dX alone, from the last micro-batch's operands (dyt and xt not given)
+    dXo = filled((M, K), torch.bfloat16, float("nan"))
+    bsq.bsq_mxfp8_backward_gemms(M, N, K, dyn=ops["dyn"], wt=ops["wt"], dX=dXo)
+    assert_bytes_equal(host(dXo).view(np.uint16), host(dX1).view(np.uint16), "dX alone")
+
+
 # ------------------------------------------------- 128-row tile variant ---
 # Products with 64..134 tiles of 256 x 256 run on 256 x 128-row tiles; these
 # shapes land there, with a ragged last tile row.
