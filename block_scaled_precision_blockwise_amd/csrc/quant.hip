@@ -260,9 +260,14 @@ __device__ __forceinline__ float int8_scale(float amax) {
   return amax == 0.f ? 1.0f : amax / 127.0f;
 }
 
-// round(x / s) with ties to even, clamped to +-127 (r = 1 / s).
+// round(x / s) with ties to even, clamped to +-127 (r = 1 / s).  The
+// Markstein quotient q1 is correctly rounded except where |x * r| < 2^-11
+// (possible underflow); there |q1| < 2^-10 all the same and rounds to the
+// integer 0, so no special case is needed for integer codes.
 __device__ __forceinline__ int32_t int8_code(float x, float s, float r) {
-  return int32_t(fminf(fmaxf(__builtin_rintf(quot(x, s, r)), -127.f), 127.f));
+  const float q0 = x * r;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
+  return int32_t(fminf(fmaxf(__builtin_rintf(q1), -127.f), 127.f));
 }
 
 __device__ __forceinline__ uint32_t int8_pack4(float4 v, float s, float r) {
@@ -498,6 +503,113 @@ __global__ void __launch_bounds__(256) k_int8_col_scales(const uint32_t* __restr
   if (j < n) ws[j] = int8_scale(__uint_as_float(cmax[j]));
 }
 
+// One pass over w when a whole column stripe fits in a workgroup's
+// registers (D_out % 16 == 0, D_in <= 4096): workgroup = one 16-column
+// stripe, all rows.  Thread t owns float4 column q4 = t & 3 of the stripe
+// and rows 512 p + 4 g + k (g = t >> 2, k < 4, p < 8): 32 float4 in
+// registers from one read of w.  The column maxima are reduced in the
+// workgroup (shuffles over the 16 lanes of a wave that share q4, then LDS
+// across the 8 waves), so no second read and no atomics.  A thread's 4
+// consecutive rows of one column pack into one word of the transposed copy.
+// Workgroups are dealt to the 8 XCDs by linear id, L % 8; XCD x takes a
+// contiguous run of S stripes, consecutive stripes on workgroups L, L + 8,
+// ...  So the two 64-byte halves of each 128-byte line of w are read
+// through one L2 at about the same time, the eight 16-byte pieces of each
+// 128-byte line of w_q meet in that L2 before they are written back, and
+// each XCD's share of a row is a contiguous 2 KiB (at D_out = 4096), which
+// spans all of its L2 channels (a 512-byte share did not).
+constexpr int kOnePassMaxRows = 4096;
+__global__ void __launch_bounds__(512) k_int8_cols_onepass(const float* __restrict__ w,
+                                                           int8_t* __restrict__ wq,
+                                                           float* __restrict__ ws,
+                                                           int8_t* __restrict__ wqT, int64_t D_in,
+                                                           int64_t D_out) {
+  __shared__ float4 red[8][4];
+  const int tx = threadIdx.x;
+  // workgroup L runs on XCD L % 8; XCD x takes stripes [S x, S x + S)
+  const int L = blockIdx.x;
+  const int64_t S = gridDim.x / 8;
+  const int64_t stripe = S * (L % 8) + L / 8;
+  if (16 * stripe >= D_out) return;
+  const int q4 = tx & 3, g = tx >> 2;
+  const int64_t j = 16 * stripe + 4 * q4;
+  const int rows = int(D_in);  // <= 4096
+  // rows past D_in re-read the last row and are zeroed afterwards, so no
+  // branch separates the loads; they go out in batches of 8 with at most
+  // 16 in flight per thread, which keeps the paired half-lines of one XCD
+  // inside its L2 until both halves are read
+  float4 v[32];
+#pragma unroll
+  for (int bt = 0; bt < 4; ++bt) {
+#pragma unroll
+    for (int n = 8 * bt; n < 8 * bt + 8; ++n) {
+      const int i = 512 * (n >> 2) + 4 * g + (n & 3);
+      v[n] = *reinterpret_cast<const float4*>(w + int64_t(min(i, rows - 1)) * D_out + j);
+    }
+    if (bt > 0) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): batch bt - 1 has landed
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    const int i = 512 * (n >> 2) + 4 * g + (n & 3);
+    if (i >= rows) v[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    m.x = fmaxf(m.x, fabsf(v[n].x));
+    m.y = fmaxf(m.y, fabsf(v[n].y));
+    m.z = fmaxf(m.z, fabsf(v[n].z));
+    m.w = fmaxf(m.w, fabsf(v[n].w));
+  }
+#pragma unroll
+  for (int off = 4; off < 64; off <<= 1) {
+    m.x = fmaxf(m.x, __shfl_xor(m.x, off));
+    m.y = fmaxf(m.y, __shfl_xor(m.y, off));
+    m.z = fmaxf(m.z, __shfl_xor(m.z, off));
+    m.w = fmaxf(m.w, __shfl_xor(m.w, off));
+  }
+  if ((tx & 63) < 4) red[tx >> 6][q4] = m;
+  __syncthreads();
+  m = red[0][q4];
+#pragma unroll
+  for (int wv = 1; wv < 8; ++wv) {
+    const float4 o = red[wv][q4];
+    m.x = fmaxf(m.x, o.x);
+    m.y = fmaxf(m.y, o.y);
+    m.z = fmaxf(m.z, o.z);
+    m.w = fmaxf(m.w, o.w);
+  }
+  const float s[4] = {int8_scale(m.x), int8_scale(m.y), int8_scale(m.z), int8_scale(m.w)};
+  const float r[4] = {1.0f / s[0], 1.0f / s[1], 1.0f / s[2], 1.0f / s[3]};
+  if (g == 0) *reinterpret_cast<float4*>(ws + j) = make_float4(s[0], s[1], s[2], s[3]);
+  int8_t* const wq_t = wq + int64_t(4 * g) * D_out + j;  // row 4 g of this thread's columns
+  int8_t* const wqT_t = wqT != nullptr ? wqT + j * D_in + 4 * g : nullptr;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (512 * p >= rows) break;
+    const bool in = 512 * p + 4 * g < rows;  // D_in % 4 == 0: the 4 rows go together
+    uint32_t col[4] = {0u, 0u, 0u, 0u};     // column q's codes of this thread's 4 rows
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 x = v[4 * p + k];
+      const float e[4] = {x.x, x.y, x.z, x.w};
+      uint32_t row = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t c = uint32_t(int8_code(e[q], s[q], r[q])) & 0xFFu;
+        row |= c << (8 * q);
+        col[q] |= c << (8 * k);
+      }
+      if (in) *reinterpret_cast<uint32_t*>(wq_t + int64_t(512 * p + k) * D_out) = row;
+    }
+    if (wqT_t != nullptr && in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(wqT_t + int64_t(q) * D_in + 512 * p) = col[q];
+    }
+  }
+}
+
 int grid_for(int64_t work_items, int per_wg) {
   int64_t g = (work_items + per_wg - 1) / per_wg;
   // a few waves of workgroups per CU is enough for a streaming kernel
@@ -592,6 +704,12 @@ bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, fl
 bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* wq, float* ws,
                             int8_t* wqT, hipStream_t st) {
   if (D_out == 0) return ok();
+  if (D_in > 0 && D_in <= kOnePassMaxRows && D_in % 4 == 0 && D_out % 16 == 0) {
+    const int64_t stripes = D_out / 16;
+    hipLaunchKernelGGL(k_int8_cols_onepass, unsigned((stripes + 7) / 8 * 8), 512, 0, st, w, wq, ws, wqT,
+                       D_in, D_out);
+    return launch_status("int8_quant_cols");
+  }
   uint32_t* cmax = reinterpret_cast<uint32_t*>(ws);  // column maxima live in w_s until the end
   hipLaunchKernelGGL(k_fill_u32, grid_for(D_out, 256), 256, 0, st, cmax, D_out, 0u);
   if (D_in > 0) {

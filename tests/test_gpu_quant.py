@@ -181,8 +181,13 @@ def test_int8_worked_examples_on_gpu(i):
     assert np.all(np.abs(host(y) - yp) <= 5e-7 + 1e-7 * np.abs(yp))
 
 
-@pytest.mark.parametrize("B,Din,Dout", [(2048, 4096, 4096), (5, 63, 6), (33, 130, 17), (7, 256, 48)])
+@pytest.mark.parametrize("B,Din,Dout", [(2048, 4096, 4096), (5, 63, 6), (33, 130, 17), (7, 256, 48),
+                                        (3, 1000, 336), (2, 4, 16), (4, 4100, 64), (3, 4096, 4112)])
 def test_int8_quantizers(B, Din, Dout):
+    """Both column paths: one pass over w (D_out % 16 == 0, D_in <= 4096,
+    D_in % 4 == 0: whole 16-column stripes per workgroup, partial row
+    passes, a partial block of 16 stripes) and the two-pass path (the
+    rest)."""
     torch = _torch()
     say("int8 quant", B, Din, Dout)
     x, w = synth.int8_workload(B, Din, Dout, 10, 11, zero_rows=(1, 7, 1000), zero_cols=(0, 3, 2047))
