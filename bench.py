@@ -354,6 +354,18 @@ def run_suite(args):
         ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(a, b, sa, sb, y), n_it)
         mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} g128 f32 out", ms, 2 * M * N * K, PEAK_FP8_TFLOPS)
         del a, b, sa, sb, y
+    # ---- general groups (the same kernel, general scale indexing)
+    M = N = K = 4096
+    a = torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev)
+    b = torch.randint(0, 126, (N, K), dtype=torch.uint8, device=dev)
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    for gn, gk in ((128, 256), (64, 128)):
+        sa = torch.rand(M, K // gk, device=dev)
+        sb = torch.rand(N // gn, K // gk, device=dev)
+        ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(a, b, sa, sb, y, group_n=gn, group_k=gk), 20)
+        mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} group_n {gn} group_k {gk} f32 out", ms, 2 * M * N * K,
+                 PEAK_FP8_TFLOPS)
+    del a, b, sa, sb, y
     # ---- INT8 per-channel
     B, Din, Dout = 2048, 4096, 4096
     x = torch.randn(B, Din, device=dev)
@@ -388,6 +400,13 @@ def run_suite(args):
                                                        lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3,
                                                        scale_dtype=bsq.BSQ_E8M0), 10)
     mfma_row("gemm_mx_batched", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/32 f32 out", ms, 2 * Bt * M * N * K,
+             PEAK_FP8_TFLOPS)
+    sa64 = torch.randint(124, 131, (Bt, M, K // 64), dtype=torch.uint8, device=dev)
+    sb64 = torch.randint(124, 131, (Bt, N, K // 64), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_scaled_matmul(lq.view(Bt, M, K), rq.view(Bt, N, K), sa64, sb64, ym,
+                                                       lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3,
+                                                       scale_dtype=bsq.BSQ_E8M0), 10)
+    mfma_row("gemm_mx_batched", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/64 f32 out", ms, 2 * Bt * M * N * K,
              PEAK_FP8_TFLOPS)
     del lhs32, lq, ls, rq, ym
     # ---- MXFP8 backward

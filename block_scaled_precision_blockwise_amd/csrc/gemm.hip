@@ -50,6 +50,10 @@ struct GemmArgs {
   int32_t* acc_out;
   int M, N, K;
   int64_t sA, sB, sSA, sSB, sC;  // batch strides in elements of each array
+  // general scale blocks (GEN kernels only): scale columns per row of A and
+  // B, K-steps of 128 (FP8G) or 32-element blocks (MX) per scale, and B
+  // rows (output columns) per B scale row (FP8G)
+  int sc_a, sc_b, sg_a, sg_b, gn;
 };
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int off0, int off1) {
@@ -222,10 +226,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
 // (Measured alternatives that were not faster: 4 waves of 128 x 128 with
 // AGPR accumulators; two wave groups alternating between MFMA and memory
 // phases with a barrier per phase; an L2 prefetch two steps ahead.)
-template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM>
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM, int GEN = 0>
 __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   static_assert(NW == 8, "8 waves: the wave layout, scale staging and epilogue assume it");
   static_assert(TBM == 256 || TBM == 128, "tile rows");
+  static_assert(!GEN || MODE != MODE_I8, "general blocks: FP8G or MX");
   constexpr int NT = 64 * NW;          // threads
   constexpr int WGM = 4;                // waves along M
   constexpr int MB = TBM / WGM / 16;    // 16-row blocks per wave along M
@@ -304,7 +309,28 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   const uint8_t* sbase = nullptr;  // this wave's scale array at K-step 0
   int soff_v = 0;                  // this lane's byte offset in it
   int64_t s_records = 0;
-  if (kScales) {
+  int s_per = 1;                   // GEN: this wave's K-steps (FP8G) / 32-blocks (MX) per scale
+  if (kScales && GEN) {
+    // general blocks: a scale row holds sc scales; B rows of the FP8G
+    // kernel are output columns, gn of them per scale row
+    const bool a_side = w < 4;
+    const int r = tid - 256;
+    const int esz = MODE == MODE_FP8G ? 4 : 1;
+    const int cols = a_side ? p.sc_a : p.sc_b;
+    s_per = a_side ? p.sg_a : p.sg_b;
+    const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + int64_t(batch) * p.sSA * esz;
+    const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + int64_t(batch) * p.sSB * esz;
+    const int rows_b = MODE == MODE_FP8G ? N / p.gn : N;
+    sbase = a_side ? SA : SB;
+    s_records = (a_side ? int64_t(M) : int64_t(rows_b)) * cols * esz;
+    // B rows: MX per column; FP8G per column (GN1) or, when group_n is a
+    // multiple of 128, per 128-column half of the tile (slots 256, 257)
+    const int row_b = MODE == MODE_MX ? min(n0 + r, N - 1)
+                      : GN1 ? min(n0 + r, N - 1) / p.gn
+                            : ((r >= 0 && r < 2 && n0 + 128 * r < N) ? (n0 + 128 * r) / p.gn : 0);
+    const int row = a_side ? min(m0 + tid, M - 1) : row_b;
+    soff_v = row * cols * esz;
+  } else if (kScales) {
     // waves 0-3 (uniform w < 4) own the A slots, waves 4-7 the B slots
     const bool a_side = w < 4;
     const int r = tid - 256;
@@ -328,9 +354,13 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       __builtin_amdgcn_readfirstlane(lds_addr_of(reinterpret_cast<const uint8_t*>(&lds_s[0][64 * w * kSG])));
   // group q (steps kSG q .. kSG q + kSG - 1) into buffer q & 1; words past a
   // row's last step are never read
+  // GEN: the 16 bytes start at the first scale the group needs (FP8G: a
+  // float, 4 per load; MX: its e8m0 byte rounded down to a word, so the
+  // group's at most 12 distinct bytes fit)
   auto sload = [&](int q) {
     if (kScales) {
-      const int64_t o = 4 * int64_t(kSG) * q;
+      const int64_t o = !GEN ? 4 * int64_t(kSG) * q
+                             : (MODE == MODE_FP8G ? 4 * int64_t((kSG * q) / s_per) : int64_t(((16 * q) / s_per) & ~3));
       lds_dma16(raw_rsrc(sbase + o, s_records - o), soff_v, ls_base + uint32_t((q & 1) * 512 * kSG * 4));
     }
   };
@@ -370,6 +400,22 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     const uint8_t* ta = lds_a + st * TBM * BK;
     const uint8_t* tb = lds_b + st * BN * BK;
     const uint32_t* ss = &lds_s[(ks / kSG) & 1][ks % kSG];  // + slot * kSG
+    // GEN, FP8G: word of this step's A / B scale within the group's 4;
+    // MX: byte of this lane's 32-block scale within the group's 16
+    const uint32_t* ssa = ss;
+    const uint32_t* ssb = ss;
+    int mxa = 0, mxb = 0;
+    if (GEN) {
+      const int q = ks / kSG;
+      if (MODE == MODE_FP8G) {
+        ssa = &lds_s[q & 1][ks / p.sg_a - (kSG * q) / p.sg_a];
+        ssb = &lds_s[q & 1][ks / p.sg_b - (kSG * q) / p.sg_b];
+      } else {
+        ssa = ssb = &lds_s[q & 1][0];
+        mxa = (4 * ks + g) / p.sg_a - (((16 * q) / p.sg_a) & ~3);
+        mxb = (4 * ks + g) / p.sg_b - (((16 * q) / p.sg_b) & ~3);
+      }
+    }
     // LDS reads retire in order, so a wait for one read also waits for all
     // reads issued before it.  The step's scales are therefore read first,
     // then the fragments in the order their MFMAs need them (the first MFMA
@@ -388,13 +434,13 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     float sbg = 0.f;
     if (MODE == MODE_FP8G) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) sa[i] = __uint_as_float(ss[(16 * MB * wm + 16 * i + r16) * kSG]);
-      if (!GN1) sbg = __uint_as_float(ss[(256 + wn) * kSG]);
+      for (int i = 0; i < MB; ++i) sa[i] = __uint_as_float(ssa[(16 * MB * wm + 16 * i + r16) * kSG]);
+      if (!GN1) sbg = __uint_as_float(ssb[(256 + wn) * kSG]);
     } else if (MODE == MODE_MX) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) qa_w[i] = ss[(16 * MB * wm + 16 * i + r16) * kSG];
+      for (int i = 0; i < MB; ++i) qa_w[i] = ssa[(16 * MB * wm + 16 * i + r16) * kSG + (GEN ? mxa >> 2 : 0)];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) qb_w[j] = ss[(256 + 128 * wn + 16 * j + r16) * kSG];
+      for (int j = 0; j < NB; ++j) qb_w[j] = ssb[(256 + 128 * wn + 16 * j + r16) * kSG + (GEN ? mxb >> 2 : 0)];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the scale reads ahead of the fragment reads
     constexpr int PF = 2;  // B fragments in flight ahead of their MFMAs
@@ -432,7 +478,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
         float sb4[4] = {0.f, 0.f, 0.f, 0.f};
         if (GN1) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sb4[r] = __uint_as_float(ss[(256 + 128 * wn + 16 * j + 4 * g + r) * kSG]);
+          for (int r = 0; r < 4; ++r) sb4[r] = __uint_as_float(ssb[(256 + 128 * wn + 16 * j + 4 * g + r) * kSG]);
         }
         v4f dcur[MB];
 #pragma unroll
@@ -448,11 +494,12 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       } else if (MODE == MODE_MX) {
         // E8M0 scale bytes: byte g of the row's word covers this lane's
         // 32-element K block (the instruction reads its scale from byte 0)
-        const int qb = int((qb_w[j] >> (8 * g)) & 0xFFu);
+        const int sha = GEN ? 8 * (mxa & 3) : 8 * g, shb = GEN ? 8 * (mxb & 3) : 8 * g;
+        const int qb = int((qb_w[j] >> shb) & 0xFFu);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              pb, q[i], acc[j][i], FB, FA, 0, qb, 0, int((qa_w[i] >> (8 * g)) & 0xFFu));
+              pb, q[i], acc[j][i], FB, FA, 0, qb, 0, int((qa_w[i] >> sha) & 0xFFu));
       } else {
         const v4i plo = {pb[0], pb[1], pb[2], pb[3]};
         const v4i phi = {pb[4], pb[5], pb[6], pb[7]};
@@ -682,9 +729,15 @@ constexpr int64_t kHalfTiles = 134;
 // (the big-tile kernel would leave most of the 256 CUs idle).
 constexpr int64_t kSkinnyTiles = 64;
 
-template <int MODE, int OUT_BF16, int FA, int FB, int GN1>
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int GEN = 0>
 bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   const int64_t tiles = int64_t((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * batch;
+  if constexpr (GEN != 0) {
+    // general scale blocks: the big-tile kernel at every size
+    dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
+    hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1>), grid, 512, 0, st, a);
+    return launch_status("gemm (general scale blocks)");
+  }
   if (tiles < kSkinnyTiles && !GN1) {
     dim3 grid(unsigned((a.N + SK_T - 1) / SK_T), unsigned((a.M + SK_T - 1) / SK_T), unsigned(batch));
     hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB>), grid, 64 * SKW, 0, st, a);
@@ -752,6 +805,31 @@ bsq_status launch_gemm(const GemmLaunch& L, hipStream_t st) {
   a.sA = L.M * L.K;
   a.sB = L.N * L.K;
   a.sC = L.M * L.N;
+  a.sc_a = L.sc_a; a.sc_b = L.sc_b; a.sg_a = L.sg_a; a.sg_b = L.sg_b; a.gn = L.gn;
+  if (L.gen && L.mode == MODE_FP8G) {
+    a.sSA = L.M * L.sc_a;
+    a.sSB = (L.N / L.gn) * L.sc_b;
+    if (L.gn % 128 == 0)  // one B scale per wave's 128 columns
+      return L.out_bf16 ? run<MODE_FP8G, 1, 0, 0, 0, 1>(a, int(L.batch), st)
+                        : run<MODE_FP8G, 0, 0, 0, 0, 1>(a, int(L.batch), st);
+    return L.out_bf16 ? run<MODE_FP8G, 1, 0, 0, 1, 1>(a, int(L.batch), st)
+                      : run<MODE_FP8G, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+  }
+  if (L.gen && L.mode == MODE_MX) {
+    a.sSA = L.M * L.sc_a;
+    a.sSB = L.N * L.sc_b;
+    const int sel = (L.fa_e5m2 ? 1 : 0) | (L.fb_e5m2 ? 2 : 0) | (L.out_bf16 ? 4 : 0);
+    switch (sel) {
+      case 0: return run<MODE_MX, 0, 0, 0, 0, 1>(a, int(L.batch), st);
+      case 1: return run<MODE_MX, 0, 1, 0, 0, 1>(a, int(L.batch), st);
+      case 2: return run<MODE_MX, 0, 0, 1, 0, 1>(a, int(L.batch), st);
+      case 3: return run<MODE_MX, 0, 1, 1, 0, 1>(a, int(L.batch), st);
+      case 4: return run<MODE_MX, 1, 0, 0, 0, 1>(a, int(L.batch), st);
+      case 5: return run<MODE_MX, 1, 1, 0, 0, 1>(a, int(L.batch), st);
+      case 6: return run<MODE_MX, 1, 0, 1, 0, 1>(a, int(L.batch), st);
+      default: return run<MODE_MX, 1, 1, 1, 0, 1>(a, int(L.batch), st);
+    }
+  }
   switch (L.mode) {
     case MODE_FP8G:
       a.sSA = L.M * (L.K / 128);

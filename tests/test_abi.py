@@ -83,7 +83,9 @@ def test_blockwise_validation(L):
     args = (A16, A16, A16, A16, A16, bsq.BSQ_F32, None)
     _expect(f(16, 256, 200, 128, 128, *args), SHAPE, L)        # K % group_k
     _expect(f(16, 200, 256, 128, 128, *args), SHAPE, L)        # N % group_n
-    _expect(f(16, 256, 256, 64, 128, *args), UNSUP, L)         # group_n 64
+    _expect(f(16, 256, 256, 128, 64, *args), UNSUP, L)         # group_k 64
+    _expect(f(16, 256, 512, 64, 256, *args), DEVICE, L)        # group_n 64, group_k 256
+    _expect(f(16, 240, 384, 48, 384, *args), DEVICE, L)        # group_n 48, group_k 384
     _expect(f(16, 256, 256, 128, 128, A16, A16, A16, A16, A16, bsq.BSQ_I8, None), UNSUP, L)
     _expect(f(16, 256, 256, 128, 128, A16, A16, A16, A16, A16, 42, None), DTYPE, L)
     _expect(f(0, 256, 256, 128, 128, None, None, None, None, None, bsq.BSQ_F32, None), OK, L)
@@ -103,6 +105,12 @@ def test_scaled_matmul_validation(L):
     _expect(f(1, 8, 16, 256, 2, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), DEVICE, L)
     _expect(f(1, 8, 16, 256, 2, 2, A16, E5, A16, E4, A16, A16, F32, A16, F32, None), UNSUP, L)
     _expect(f(1, 8, 16, 128, 4, 4, A16, E4, A16, E4, A4 + 1, A16, E8, A16, F32, None), ALIGN, L)
+    # general blocks: E8M0 multiples of 32 (K_a != K_b allowed; rows of a
+    # multiple of 4 scales), F32 multiples of 128
+    _expect(f(1, 8, 16, 512, 8, 16, A16, E4, A16, E5, A16, A16, E8, A16, F32, None), DEVICE, L)
+    _expect(f(1, 8, 16, 256, 2, 8, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
+    _expect(f(1, 8, 16, 768, 3, 6, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), DEVICE, L)
+    _expect(f(1, 8, 16, 256, 4, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), UNSUP, L)
 
 
 def test_int8_validation(L):

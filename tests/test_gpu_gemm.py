@@ -64,11 +64,12 @@ def _blockwise_hw_bound(a, b, sa, sb):
     return fp8_group_bound(A, Bv)
 
 
-def _run_blockwise(a, b, sa, sb, out_dtype=None, group_n=128):
+def _run_blockwise(a, b, sa, sb, out_dtype=None, group_n=128, group_k=128):
     torch = _torch()
     M, N = a.shape[0], b.shape[0]
     y = filled((M, N), out_dtype or torch.float32, float("nan"))
-    bsq.bsq_blockwise_fp8_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, group_n=group_n)
+    bsq.bsq_blockwise_fp8_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, group_n=group_n,
+                                 group_k=group_k)
     return y
 
 
@@ -190,6 +191,86 @@ def test_blockwise_group_n_1_via_scaled_matmul_f32():
     b, sb = OQ.fp8_rowblock(synth.randn_f32((Bt * N, K), 42))
     a, sa = a.reshape(Bt, M, K), sa.reshape(Bt, M, K // 128)
     b, sb = b.reshape(Bt, N, K), sb.reshape(Bt, N, K // 128)
+    y = filled((Bt, M, N), torch.float32, float("nan"))
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y,
+                          lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_F32)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, "e4m3", "e4m3", "f32")
+    assert_within_T(host(y), yr, T, "y")
+
+
+# --------------------------------------- general blocks (NEXT: groups) ---
+# block_scaled_mm with group_n, group_k other than (128 | 1, 128), and
+# scaled_matmul with lhs and rhs blocks of different sizes (the pages allow
+# any block dividing K); the same kernel with general scale indexing.
+
+@pytest.mark.parametrize("M,N,K,gn,gk", [(300, 384, 768, 64, 256), (257, 240, 1152, 48, 384),
+                                         (513, 512, 1024, 256, 512), (130, 272, 640, 16, 128),
+                                         (200, 256, 512, 1, 256), (200, 384, 512, 128, 256)])
+def test_blockwise_general_groups(M, N, K, gn, gk):
+    torch = _torch()
+    say("blockwise general groups", M, N, K, gn, gk)
+    a, _ = OQ.fp8_rowblock(synth.randn_f32((M, K), 800 + M))
+    b, _ = OQ.fp8_rowblock(synth.randn_f32((N, K), 801 + M))
+    sa = synth.random_f32_scales((M, K // gk), 802 + M)
+    sb = synth.random_f32_scales((N // gn, K // gk), 803 + M)
+    for od in (torch.float32, torch.bfloat16):
+        y = _run_blockwise(a, b, sa, sb, od, group_n=gn, group_k=gk)
+        yr, T = OM.blockwise_fp8(a, b, sa, sb, group_n=gn, group_k=gk)
+        yh = host(y) if od == torch.float32 else OF.decode_bf16(host(y))
+        assert_within_T(yh, yr, T, f"y {od}", bf16=(od == torch.bfloat16))
+
+
+def test_blockwise_general_groups_full_size_sampled():
+    """m = n = k = 4096 with group_n 64, group_k 256: sampled rows."""
+    torch = _torch()
+    M = N = K = 4096
+    gn, gk = 64, 256
+    say("blockwise general groups full size", M, N, K, gn, gk)
+    a, b, _, _ = _random_blockwise(M, N, K, 830)
+    sa = synth.random_f32_scales((M, K // gk), 831)
+    sb = synth.random_f32_scales((N // gn, K // gk), 832)
+    y = host(_run_blockwise(a, b, sa, sb, group_n=gn, group_k=gk))
+    rows = _rows_sample(M, seed=5)
+    yr, T = OM.blockwise_fp8(a[rows], b, sa[rows], sb, group_n=gn, group_k=gk)
+    A = np.abs(OF.decode(a[rows], "e4m3")) * np.repeat(sa[rows].astype(np.float64), gk, axis=1)
+    Bv = np.abs(OF.decode(b, "e4m3")) * np.repeat(np.repeat(sb.astype(np.float64), gn, axis=0), gk, axis=1)
+    assert_within_T_hw(y[rows], yr, T, fp8_group_bound(A, Bv), "y rows")
+    assert np.all(np.isfinite(y)), "unwritten output"
+
+
+@pytest.mark.parametrize("Bt,M,N,K,ba,bb,lf,rf,out", [
+    (2, 100, 272, 512, 64, 32, "e4m3", "e5m2", "f32"),
+    (2, 130, 144, 1024, 128, 256, "e5m2", "e5m2", "bf16"),
+    (1, 64, 64, 768, 96, 64, "e4m3", "e4m3", "f32"),
+])
+def test_scaled_matmul_e8m0_general_blocks(Bt, M, N, K, ba, bb, lf, rf, out):
+    """E8M0 scales with blocks K / K_a != K / K_b (multiples of 32)."""
+    torch = _torch()
+    say("scaled_matmul e8m0 blocks", Bt, M, N, K, ba, bb)
+    a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 810 + ba), lf)
+    b, _ = OQ.mx(synth.randn_f32((Bt, N, K), 811 + bb), rf)
+    sa = synth.random_e8m0_codes((Bt, M, K // ba), 812)
+    sb = synth.random_e8m0_codes((Bt, N, K // bb), 813)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = filled((Bt, M, N), od, float("nan"))
+    code = {"e4m3": bsq.BSQ_E4M3, "e5m2": bsq.BSQ_E5M2}
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=code[lf],
+                          rhs_dtype=code[rf], scale_dtype=bsq.BSQ_E8M0)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, lf, rf, "e8m0")
+    yh = host(y) if out == "f32" else OF.decode_bf16(host(y))
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
+
+
+@pytest.mark.parametrize("Bt,M,N,K,ba,bb", [(2, 70, 144, 768, 256, 128), (1, 100, 256, 1536, 384, 512)])
+def test_scaled_matmul_f32_general_blocks(Bt, M, N, K, ba, bb):
+    """float32 scales with blocks K / K_a != K / K_b (multiples of 128)."""
+    torch = _torch()
+    say("scaled_matmul f32 blocks", Bt, M, N, K, ba, bb)
+    a, _ = OQ.fp8_rowblock(synth.randn_f32((Bt * M, K), 820 + ba))
+    b, _ = OQ.fp8_rowblock(synth.randn_f32((Bt * N, K), 821 + bb))
+    a, b = a.reshape(Bt, M, K), b.reshape(Bt, N, K)
+    sa = synth.random_f32_scales((Bt, M, K // ba), 822)
+    sb = synth.random_f32_scales((Bt, N, K // bb), 823)
     y = filled((Bt, M, N), torch.float32, float("nan"))
     bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y,
                           lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_F32)
