@@ -16,9 +16,12 @@ these names refer to:
           max 57344
   e8m0fnu eeeeeeee,   value 2^(e-127), 0xFF is NaN, no sign, no zero
   bf16    the upper 16 bits of an IEEE binary32.
+  e2m1fn  s.ee.m, bias 1, no infinities or NaN, max 6 (nvfp4 operands,
+          jax.nn.scaled_matmul Notes; with float8_e4m3fn scales, block 16).
 
 Pins: tests/test_oracle_formats.py compares every decode with torch's CPU
-float8/bfloat16 views, and every encode with torch's CPU casts on all
+float8/bfloat16 views (e2m1, which torch cannot convert, through the
+pinned e4m3 codec: every e2m1 value is an e4m3 value, plus its invariants), and every encode with torch's CPU casts on all
 midpoints (and one float32 ulp either side) plus random values, over the
 clamped domain the method uses.
 """
@@ -110,6 +113,41 @@ def decode_e8m0(codes: np.ndarray) -> np.ndarray:
     b = np.asarray(codes, dtype=np.int64)
     out = np.ldexp(1.0, b - 127)
     return np.where(b == 255, np.nan, out)
+
+
+# ----------------------------------------------------------------- e2m1 ----
+# float4_e2m1fn (named by jax.nn.scaled_matmul's Notes for nvfp4 operands;
+# bits from the OCP 4-bit definition): s.ee.m, exponent bias 1, no
+# infinities or NaN; exponent 0 is subnormal (m * 0.5).  Magnitudes 0, 0.5,
+# 1, 1.5, 2, 3, 4, 6.  Packed two to a byte, the element with the lower
+# index in the low nibble.
+
+E2M1 = "e2m1"
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes (0..15, one per array element) to float64."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return sign * mag
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """[..., K] codes (K even) -> [..., K/2] bytes, low nibble first."""
+    c = np.asarray(codes, dtype=np.uint8) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_e2m1(packed: np.ndarray) -> np.ndarray:
+    """[..., K/2] bytes -> [..., K] codes, low nibble first."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
 
 
 # ----------------------------------------------------------------- bf16 ----

@@ -44,6 +44,8 @@ from . import formats as F
 def _dec_operand(codes: np.ndarray, fmt: str) -> np.ndarray:
     if fmt in (F.E4M3, F.E5M2):
         return F.decode(codes, fmt)
+    if fmt == F.E2M1:  # one 4-bit code per element (unpacked)
+        return F.decode_e2m1(codes)
     if fmt == "f32":
         return np.asarray(codes, dtype=np.float32).astype(np.float64)
     if fmt == "f64":

@@ -85,6 +85,22 @@ def random_e8m0_codes(shape, seed: int, lo: int = -3, hi: int = 3) -> np.ndarray
     return (127 + j).astype(np.uint8)
 
 
+def random_e2m1_codes(shape, seed: int) -> np.ndarray:
+    """Uniformly random 4-bit codes 0..15, one per element."""
+    return rng(seed).integers(0, 16, size=tuple(shape)).astype(np.uint8)
+
+
+def random_e4m3_scale_codes(shape, seed: int, e_lo: int = 4, e_hi: int = 10) -> np.ndarray:
+    """Positive normal e4m3fn bytes: exponent field uniform on e_lo..e_hi,
+    mantissa field uniform on 0..7 (never the NaN code)."""
+    if not 0 <= e_lo <= e_hi <= 14:
+        raise ValueError("exponent fields 0..14 (15 with mantissa 7 is NaN)")
+    g = rng(seed)
+    e = g.integers(e_lo, e_hi + 1, size=tuple(shape))
+    m = g.integers(0, 8, size=tuple(shape))
+    return ((e << 3) | m).astype(np.uint8)
+
+
 def random_f32_scales(shape, seed: int) -> np.ndarray:
     """Positive float32 scales spread over a few binades (log-uniform)."""
     e = rng(seed).uniform(-6.0, 2.0, size=tuple(shape))

@@ -104,3 +104,45 @@ def test_bf16_codec_matches_torch():
     back = F.decode_bf16(ours)
     refd = torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(back, refd)
+
+
+# ------------------------------------------------------------- e2m1 ----
+# torch cannot convert its float4 type, so the e2m1 decoder is pinned
+# through the e4m3 codec (pinned to torch above): every e2m1 value is an
+# e4m3 value, with the exponent re-biased from 1 to 7 and the mantissa bit
+# moved to the top of e4m3's three; plus the format's invariants.
+
+def test_e2m1_values_are_e4m3_values():
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        if e == 0 and m == 0:
+            e4 = s << 7                            # signed zero
+        elif e == 0:
+            e4 = (s << 7) | (6 << 3)               # 0.5 = 2^-1, a normal e4m3
+        else:
+            e4 = (s << 7) | ((e + 6) << 3) | (m << 2)
+        want = F.decode(np.array([e4], np.uint8), F.E4M3)[0]
+        got = F.decode_e2m1(np.array([c]))[0]
+        assert got == want and np.signbit(got) == np.signbit(want), (c, got, want)
+
+
+def test_e2m1_invariants():
+    v = F.decode_e2m1(np.arange(16))
+    pos = v[:8]
+    assert list(pos) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(v[8:], -pos)               # the top bit is the sign
+    assert pos.max() == 6.0                           # 1.5 * 2^(3 - 1)
+    # every magnitude has at most two significant bits
+    for x in pos[1:]:
+        mant, _ = np.frexp(x)
+        assert (mant * 4) == int(mant * 4)
+
+
+def test_e2m1_pack_roundtrip_low_nibble_first():
+    g = np.random.default_rng(5)
+    c = g.integers(0, 16, size=(3, 7, 64)).astype(np.uint8)
+    p = F.pack_e2m1(c)
+    assert p.shape == (3, 7, 32)
+    assert np.array_equal(p[..., 0] & 0xF, c[..., 0]) and np.array_equal(p[..., 0] >> 4, c[..., 1])
+    assert np.array_equal(F.unpack_e2m1(p), c)

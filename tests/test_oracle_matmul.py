@@ -76,6 +76,30 @@ def test_scaled_matmul_exact_brute_force(lf, rf, sf, Ka, Kb):
                 assert abs(Fraction(float(T[bi, m, n])) - absum) <= Fraction(1, 10 ** 12) * absum
 
 
+def test_scaled_matmul_nvfp4_exact_brute_force():
+    """The Notes' nvfp4 combination: e2m1 operands, e4m3 scales, block 16;
+    exact rational sums on a tiny shape."""
+    B, M, N, K = 2, 3, 4, 64
+    a = synth.random_e2m1_codes((B, M, K), 31)
+    b = synth.random_e2m1_codes((B, N, K), 32)
+    sa = synth.random_e4m3_scale_codes((B, M, K // 16), 33, 1, 14)
+    sb = synth.random_e4m3_scale_codes((B, N, K // 16), 34, 1, 14)
+    y, T = MM.scaled_matmul(a, b, sa, sb, F.E2M1, F.E2M1, F.E4M3)
+    dec = {c: Fraction(float(F.decode_e2m1(np.array([c]))[0])) for c in range(16)}
+    for bi in range(B):
+        for m in range(M):
+            for n in range(N):
+                exact = Fraction(0)
+                absum = Fraction(0)
+                for k in range(K):
+                    t = (dec[int(a[bi, m, k])] * _frac_value(sa[bi, m, k // 16], F.E4M3) *
+                         dec[int(b[bi, n, k])] * _frac_value(sb[bi, n, k // 16], F.E4M3))
+                    exact += t
+                    absum += abs(t)
+                assert abs(Fraction(float(y[bi, m, n])) - exact) <= Fraction(1, 10 ** 12) * absum
+                assert abs(Fraction(float(T[bi, m, n])) - absum) <= Fraction(1, 10 ** 12) * absum
+
+
 def test_scaled_matmul_ones_scales_is_plain_matmul():
     # the pattern of the documentation's second example: all scales one
     a = synth.random_fp8_codes((3, 16, 64), 25, F.E4M3)
