@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s & % of FP8 MFMA peak, block-scaled GEMM m=n=k=4096 group 128"
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # block_scaled_mm row 14 (m = n = k = 4096): T_Prod = 1.06 ms on unstated
 # hardware, i.e. 2 * 4096^3 / 1.06 ms = 129.66 TFLOP/s (GEMM only).
@@ -366,6 +367,18 @@ def run_suite(args):
         mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} group_n {gn} group_k {gk} f32 out", ms, 2 * M * N * K,
                  PEAK_FP8_TFLOPS)
     del a, b, sa, sb, y
+    # ---- nvfp4 scaled_matmul (dequantize to bf16 + bf16 matrix core)
+    Bt, M, N, K = 1, 4096, 4096, 4096
+    a = torch.randint(0, 256, (Bt, M, K // 2), dtype=torch.uint8, device=dev)
+    b = torch.randint(0, 256, (Bt, N, K // 2), dtype=torch.uint8, device=dev)
+    sa = torch.randint(0x20, 0x50, (Bt, M, K // 16), dtype=torch.uint8, device=dev)
+    sb = torch.randint(0x20, 0x50, (Bt, N, K // 16), dtype=torch.uint8, device=dev)
+    y = torch.empty(Bt, M, N, dtype=torch.float32, device=dev)
+    wsn = torch.empty(bsq.bsq_nvfp4_workspace_bytes(Bt, M, N, K), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_scaled_matmul_nvfp4(a, b, sa, sb, y, wsn), 20)
+    mfma_row("scaled_matmul_nvfp4 (dequantize + bf16 GEMM)", f"{M}x{N}x{K} e2m1 e4m3/16 f32 out", ms,
+             2 * M * N * K, PEAK_BF16_TFLOPS)
+    del a, b, sa, sb, y, wsn
     # ---- INT8 per-channel
     B, Din, Dout = 2048, 4096, 4096
     x = torch.randn(B, Din, device=dev)

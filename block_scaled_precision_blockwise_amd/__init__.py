@@ -32,6 +32,7 @@ __all__ = [
     "bsq_int8_workspace_bytes", "bsq_int8_per_channel_matmul",
     "bsq_mxfp8_backward_workspace_bytes", "bsq_mxfp8_backward",
     "mxfp8_backward_operand_shapes", "bsq_mxfp8_backward_quantize", "bsq_mxfp8_backward_gemms",
+    "bsq_nvfp4_workspace_bytes", "bsq_scaled_matmul_nvfp4",
     "BsqError",
 ]
 
@@ -68,6 +69,8 @@ _SIGNATURES = {
                                            _P, _P]),
     "bsq_mxfp8_backward_gemms": (_INT, [_I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P]),
+    "bsq_nvfp4_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "bsq_scaled_matmul_nvfp4": (_INT, [_I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _INT, _P, _SZ, _P]),
 }
 
 
@@ -440,3 +443,33 @@ def bsq_mxfp8_backward_gemms(M: int, N: int, K: int, dyn=None, wt=None, dyt=None
     flat = [v for pr in ptrs for v in pr]
     _raise(lib().bsq_mxfp8_backward_gemms(M, N, K, code_dtype, od, *flat, _ptr(dX), _ptr(dW), _stream(stream)),
            "bsq_mxfp8_backward_gemms")
+
+
+def bsq_nvfp4_workspace_bytes(B: int, M: int, N: int, K: int) -> int:
+    return int(lib().bsq_nvfp4_workspace_bytes(B, M, N, K))
+
+
+def bsq_scaled_matmul_nvfp4(lhs, rhs, lhs_scales, rhs_scales, out, workspace, stream=None):
+    """scaled_matmul with nvfp4 operands: lhs [B, M, K/2], rhs [B, N, K/2]
+    packed e2m1 (uint8, low nibble first), scales [B, M, K/16] and
+    [B, N, K/16] e4m3 bytes; out float32 or bfloat16 [B, M, N]."""
+    torch = _torch()
+    _dev(lhs, rhs, lhs_scales, rhs_scales, out, workspace)
+    for t, n in ((lhs, "lhs"), (rhs, "rhs"), (lhs_scales, "lhs_scales"), (rhs_scales, "rhs_scales")):
+        _bytes1(t, n)
+    B, M, K2 = lhs.shape
+    N = rhs.shape[1]
+    K = 2 * K2
+    if tuple(rhs.shape) != (B, N, K2):
+        raise ValueError("rhs must be [B, N, K/2]")
+    if tuple(lhs_scales.shape) != (B, M, K // 16) or tuple(rhs_scales.shape) != (B, N, K // 16):
+        raise ValueError("scales must be [B, M, K/16] and [B, N, K/16]")
+    if tuple(out.shape) != (B, M, N):
+        raise ValueError("out must be [B, M, N]")
+    od = {torch.float32: BSQ_F32, torch.bfloat16: BSQ_BF16}.get(out.dtype)
+    if od is None:
+        raise TypeError("out must be float32 or bfloat16")
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise(lib().bsq_scaled_matmul_nvfp4(B, M, N, K, _ptr(lhs), _ptr(rhs), _ptr(lhs_scales), _ptr(rhs_scales),
+                                         _ptr(out), od, _ptr(workspace), nbytes, _stream(stream)),
+           "bsq_scaled_matmul_nvfp4")

@@ -558,4 +558,53 @@ bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dt
                    want_dw ? dW : nullptr, as_stream(stream));
 }
 
+// ------------------------------------------------------------- nvfp4 --
+
+size_t bsq_nvfp4_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K) {
+  if (B < 0 || M < 0 || N < 0 || K < 0) return 0;
+  return up256(size_t(B * M * K * 2)) + up256(size_t(B * N * K * 2));
+}
+
+bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, const uint8_t* lhs,
+                                   const uint8_t* rhs, const uint8_t* lhs_scales,
+                                   const uint8_t* rhs_scales, void* out, int out_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  BSQ_CHECK(B >= 0 && M >= 0 && N >= 0 && K >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(K % 16 == 0, BSQ_ERR_SHAPE, "K must be a multiple of the block (16)");
+  BSQ_CHECK(known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown out_dtype");
+  BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
+            "out_dtype must be F32 or BF16");
+  BSQ_CHECK(K % 128 == 0 && N % 16 == 0, BSQ_ERR_UNSUPPORTED,
+            "this build needs K % 128 == 0 and N % 16 == 0");
+  BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction / 2,
+            BSQ_ERR_UNSUPPORTED, "extent too large");
+  const size_t need = bsq_nvfp4_workspace_bytes(B, M, N, K);
+  BSQ_CHECK(workspace_bytes >= need, BSQ_ERR_SHAPE, "workspace too small");
+  if (B == 0 || M == 0 || N == 0) return ok();
+  BSQ_CHECK_PTR(out);
+  if (K > 0) {
+    BSQ_CHECK_PTR(lhs);
+    BSQ_CHECK_PTR(rhs);
+    BSQ_CHECK(lhs_scales != nullptr && rhs_scales != nullptr, BSQ_ERR_NULL, "scales are NULL");
+    BSQ_CHECK_PTR(workspace);
+  }
+  BSQ_DEVICE();
+  hipStream_t st = as_stream(stream);
+  uint16_t* wa = static_cast<uint16_t*>(workspace);
+  uint16_t* wb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + up256(size_t(B * M * K * 2)));
+  bsq_status s = BSQ_OK;
+  if (K > 0) {
+    if ((s = launch_nvfp4_to_bf16(B * M, K, lhs, lhs_scales, wa, st)) != BSQ_OK) return s;
+    if ((s = launch_nvfp4_to_bf16(B * N, K, rhs, rhs_scales, wb, st)) != BSQ_OK) return s;
+  }
+  GemmLaunch L{};
+  L.mode = MODE_BF16;
+  L.batch = B;
+  L.M = M; L.N = N; L.K = K;
+  L.A = wa; L.B = wb;
+  L.out = out;
+  L.out_bf16 = out_dtype == BSQ_BF16;
+  return launch_gemm(L, st);
+}
+
 }  // extern "C"

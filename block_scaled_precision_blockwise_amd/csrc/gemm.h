@@ -5,7 +5,9 @@
 
 namespace bsq {
 
-enum GemmMode { MODE_FP8G = 0, MODE_MX = 1, MODE_I8 = 2 };
+// MODE_BF16: bfloat16 operands without scales (the operand dequantized
+// from nvfp4), K counted in elements; float32 accumulation.
+enum GemmMode { MODE_FP8G = 0, MODE_MX = 1, MODE_I8 = 2, MODE_BF16 = 3 };
 
 struct GemmLaunch {
   int mode;          // GemmMode
@@ -29,7 +31,8 @@ struct GemmLaunch {
   int sc_a, sc_b, sg_a, sg_b, gn;
 };
 
-// Requires K % 128 == 0 and N % 16 == 0; M, N, batch >= 0.
+// Requires K % 128 == 0 (MODE_BF16: K % 64 == 0) and N % 16 == 0; M, N,
+// batch >= 0.
 bsq_status launch_gemm(const GemmLaunch& L, hipStream_t st);
 
 // Exact int8 matmul for any D_in, D_out (one thread per output): the same

@@ -37,6 +37,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
@@ -230,7 +231,7 @@ template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM, int 
 __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   static_assert(NW == 8, "8 waves: the wave layout, scale staging and epilogue assume it");
   static_assert(TBM == 256 || TBM == 128, "tile rows");
-  static_assert(!GEN || MODE != MODE_I8, "general blocks: FP8G or MX");
+  static_assert(!GEN || MODE == MODE_FP8G || MODE == MODE_MX, "general blocks: FP8G or MX");
   constexpr int NT = 64 * NW;          // threads
   constexpr int WGM = 4;                // waves along M
   constexpr int MB = TBM / WGM / 16;    // 16-row blocks per wave along M
@@ -304,7 +305,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   // Lane i of wave w fills slot 64 w + i (waves 0-3 the A rows, 4-7 the B
   // rows).  Lanes with nothing to move read row 0 of their operand's scales
   // into a slot nobody reads.
-  constexpr bool kScales = MODE != MODE_I8;
+  constexpr bool kScales = MODE == MODE_FP8G || MODE == MODE_MX;
   static_assert(!kScales || NW == 8, "scale staging assumes 512 threads");
   const uint8_t* sbase = nullptr;  // this wave's scale array at K-step 0
   int soff_v = 0;                  // this lane's byte offset in it
@@ -500,7 +501,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
         for (int i = 0; i < MB; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               pb, q[i], acc[j][i], FB, FA, 0, qb, 0, int((qa_w[i] >> sha) & 0xFFu));
-      } else {
+      } else if (MODE == MODE_I8) {
         const v4i plo = {pb[0], pb[1], pb[2], pb[3]};
         const v4i phi = {pb[4], pb[5], pb[6], pb[7]};
 #pragma unroll
@@ -509,6 +510,21 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
           const v4i qhi = {q[i][4], q[i][5], q[i][6], q[i][7]};
           acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(plo, qlo, acc[j][i], 0, 0, 0);
           acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(phi, qhi, acc[j][i], 0, 0, 0);
+        }
+      } else {
+        // bf16: each 16-byte half of a fragment is 8 elements of K (the
+        // same K positions in the A and the B fragment, so the order of K
+        // inside an instruction does not matter)
+        const v4i plo = {pb[0], pb[1], pb[2], pb[3]};
+        const v4i phi = {pb[4], pb[5], pb[6], pb[7]};
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const v4i qlo = {q[i][0], q[i][1], q[i][2], q[i][3]};
+          const v4i qhi = {q[i][4], q[i][5], q[i][6], q[i][7]};
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, plo),
+                                                              __builtin_bit_cast(bf16x8, qlo), acc[j][i], 0, 0, 0);
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, phi),
+                                                              __builtin_bit_cast(bf16x8, qhi), acc[j][i], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -738,10 +754,12 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
     hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1>), grid, 512, 0, st, a);
     return launch_status("gemm (general scale blocks)");
   }
-  if (tiles < kSkinnyTiles && !GN1) {
-    dim3 grid(unsigned((a.N + SK_T - 1) / SK_T), unsigned((a.M + SK_T - 1) / SK_T), unsigned(batch));
-    hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB>), grid, 64 * SKW, 0, st, a);
-    return launch_status("gemm (split K)");
+  if constexpr (MODE != MODE_BF16) {
+    if (tiles < kSkinnyTiles && !GN1) {
+      dim3 grid(unsigned((a.N + SK_T - 1) / SK_T), unsigned((a.M + SK_T - 1) / SK_T), unsigned(batch));
+      hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB>), grid, 64 * SKW, 0, st, a);
+      return launch_status("gemm (split K)");
+    }
   }
   constexpr int NW = 8;
   if (tiles <= kHalfTiles) {
@@ -857,6 +875,14 @@ bsq_status launch_gemm(const GemmLaunch& L, hipStream_t st) {
       a.sSA = L.M;
       a.sSB = L.N;
       return run<MODE_I8, 0, 0, 0, 0>(a, int(L.batch), st);
+    case MODE_BF16:
+      // the kernel walks rows in bytes: 2 K bytes, 64 elements per step
+      a.K = int(2 * L.K);
+      a.sA = L.M * 2 * L.K;
+      a.sB = L.N * 2 * L.K;
+      a.sSA = a.sSB = 0;
+      return L.out_bf16 ? run<MODE_BF16, 1, 0, 0, 0>(a, int(L.batch), st)
+                        : run<MODE_BF16, 0, 0, 0, 0>(a, int(L.batch), st);
   }
   return fail(BSQ_ERR_UNSUPPORTED, "unknown gemm mode");
 }

@@ -15,5 +15,9 @@ bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, fl
                             hipStream_t st);
 bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* wq, float* ws,
                             int8_t* wqT, hipStream_t st);
+// nvfp4 rows (K/2 bytes of e2m1 codes, low nibble first, and K/16 e4m3
+// scales per row) -> bf16 [rows, K]; exact.  K % 16 == 0.
+bsq_status launch_nvfp4_to_bf16(int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
+                                uint16_t* out, hipStream_t st);
 
 }  // namespace bsq

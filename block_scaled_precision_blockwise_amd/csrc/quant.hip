@@ -610,6 +610,37 @@ __global__ void __launch_bounds__(512) k_int8_cols_onepass(const float* __restri
   }
 }
 
+// ---------------------------------------------------- nvfp4 -> bf16 ----
+// One thread per block of 16 values: 8 bytes of e2m1 codes (the lower index
+// in the low nibble) and one e4m3 scale.  An e2m1 magnitude (0, 0.5, 1, 1.5,
+// 2, 3, 4, 6) times an e4m3 scale has at most 6 significant bits and lies in
+// [2^-10, 2688], so the float32 product is exact and so are its upper 16
+// bits as a bfloat16.
+__device__ __forceinline__ float e2m1_value(uint32_t nib) {
+  const uint32_t e = (nib >> 1) & 3u, m = nib & 1u;
+  const uint32_t mag = e ? (((e + 126u) << 23) | (m << 22)) : (m ? (126u << 23) : 0u);
+  return __uint_as_float(((nib & 8u) << 28) | mag);
+}
+
+__global__ void __launch_bounds__(256) k_nvfp4_to_bf16(const uint2* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       uint4* __restrict__ out, int64_t nblocks) {
+  for (int64_t b = int64_t(blockIdx.x) * 256 + threadIdx.x; b < nblocks; b += int64_t(gridDim.x) * 256) {
+    const uint2 c = codes[b];
+    const float s = __builtin_amdgcn_cvt_f32_fp8(int(scales[b]), 0);
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const uint32_t word = e < 8 ? c.x : c.y;
+      const uint32_t lo = __float_as_uint(e2m1_value((word >> (4 * (e % 8))) & 0xFu) * s) >> 16;
+      const uint32_t hi = __float_as_uint(e2m1_value((word >> (4 * (e % 8) + 4)) & 0xFu) * s) >> 16;
+      h[e / 2] = lo | (hi << 16);
+    }
+    out[2 * b] = make_uint4(h[0], h[1], h[2], h[3]);
+    out[2 * b + 1] = make_uint4(h[4], h[5], h[6], h[7]);
+  }
+}
+
 int grid_for(int64_t work_items, int per_wg) {
   int64_t g = (work_items + per_wg - 1) / per_wg;
   // a few waves of workgroups per CU is enough for a streaming kernel
@@ -729,6 +760,15 @@ bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t*
   }
   hipLaunchKernelGGL(k_int8_col_scales, unsigned((D_out + 255) / 256), 256, 0, st, cmax, ws, D_out);
   return launch_status("int8_quant_cols");
+}
+
+bsq_status launch_nvfp4_to_bf16(int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
+                                uint16_t* out, hipStream_t st) {
+  const int64_t nblocks = rows * (K / 16);
+  if (nblocks == 0) return ok();
+  hipLaunchKernelGGL(k_nvfp4_to_bf16, grid_for(nblocks, 256), 256, 0, st, reinterpret_cast<const uint2*>(codes),
+                     scales, reinterpret_cast<uint4*>(out), nblocks);
+  return launch_status("nvfp4_to_bf16");
 }
 
 }  // namespace bsq

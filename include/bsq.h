@@ -255,6 +255,25 @@ bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dt
                                     const uint8_t* xt_codes, const uint8_t* xt_scales, void* dX, void* dW,
                                     void* stream);
 
+/* scaled_matmul with nvfp4 operands (scaled_matmul, Notes: float4_e2m1fn
+ * operands, float8_e4m3fn scales, block 16; the sum as in
+ * bsq_scaled_matmul with K_a = K_b = K / 16).
+ *   lhs [B, M, K/2], rhs [B, N, K/2]: e2m1 codes, two per byte, the element
+ *       with the lower K index in the low nibble
+ *   lhs_scales [B, M, K/16], rhs_scales [B, N, K/16]: e4m3 (OCP e4m3fn)
+ *   out [B, M, N], out_dtype BSQ_F32 or BSQ_BF16
+ *   workspace: at least bsq_nvfp4_workspace_bytes(B, M, N, K) bytes; it
+ *       receives both operands dequantized to bfloat16 (exact: an e2m1
+ *       value times an e4m3 scale has at most 6 significant bits), which
+ *       a bf16 matrix-core product then multiplies in float32.
+ * Rules: K % 16 == 0 (else SHAPE); this build needs K % 128 == 0 and
+ * N % 16 == 0 (else UNSUPPORTED); a smaller workspace -> SHAPE. */
+size_t bsq_nvfp4_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K);
+bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, const uint8_t* lhs,
+                                   const uint8_t* rhs, const uint8_t* lhs_scales,
+                                   const uint8_t* rhs_scales, void* out, int out_dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -189,3 +189,18 @@ def test_backward_split_validation(L):
     _expect(g(256, 256, 256, E5, F32, *([None] * 4), A16, A16, A16, A16, None, A4, None), ALIGN, L)
     # an empty contraction needs no operands (the output is zeros)
     _expect(g(256, 0, 256, E5, BF, *([None] * 8), A16, None, None), DEVICE, L)
+
+
+def test_nvfp4_validation(L):
+    f = L.bsq_scaled_matmul_nvfp4
+    need = L.bsq_nvfp4_workspace_bytes(1, 16, 32, 256)
+    assert need >= 2 * 256 * (16 + 32)
+    F32, BF = bsq.BSQ_F32, bsq.BSQ_BF16
+    _expect(f(1, 16, 32, 200, A16, A16, A16, A16, A16, F32, A16, need, None), SHAPE, L)   # K % 16
+    _expect(f(1, 16, 32, 144, A16, A16, A16, A16, A16, F32, A16, need, None), UNSUP, L)   # K % 128
+    _expect(f(1, 16, 24, 256, A16, A16, A16, A16, A16, F32, A16, need, None), UNSUP, L)   # N % 16
+    _expect(f(1, 16, 32, 256, A16, A16, A16, A16, A16, bsq.BSQ_I8, A16, need, None), UNSUP, L)
+    _expect(f(1, 16, 32, 256, A16, A16, A16, A16, A16, F32, A16, need - 1, None), SHAPE, L)
+    _expect(f(1, 16, 32, 256, A16, A16, None, A16, A16, F32, A16, need, None), NULL, L)
+    _expect(f(0, 16, 32, 256, None, None, None, None, None, F32, None, 0, None), OK, L)
+    _expect(f(1, 16, 32, 256, A16, A16, A16, A16, A16, BF, A16, need, None), DEVICE, L)

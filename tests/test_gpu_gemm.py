@@ -278,6 +278,65 @@ def test_scaled_matmul_f32_general_blocks(Bt, M, N, K, ba, bb):
     assert_within_T(host(y), yr, T, "y")
 
 
+# ------------------------------------------------------ nvfp4 (NEXT) -----
+# scaled_matmul's nvfp4 combination: e2m1 operands (two per byte, the lower
+# K index in the low nibble), e4m3 scales per 16.  The library dequantizes
+# both operands to bfloat16 in the caller's workspace (exact) and multiplies
+# them on the bf16 matrix core.
+
+def _pack_nibbles(codes):
+    c = np.asarray(codes, np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _run_nvfp4(a, b, sa, sb, out_dtype):
+    torch = _torch()
+    Bt, M, K = a.shape
+    N = b.shape[1]
+    y = filled((Bt, M, N), out_dtype, float("nan"))
+    ws = empty((bsq.bsq_nvfp4_workspace_bytes(Bt, M, N, K),), torch.uint8)
+    bsq.bsq_scaled_matmul_nvfp4(to_dev(_pack_nibbles(a)), to_dev(_pack_nibbles(b)), to_dev(sa), to_dev(sb), y, ws)
+    return y, ws
+
+
+@pytest.mark.parametrize("Bt,M,N,K,out", [(2, 100, 272, 512, "f32"), (1, 257, 144, 384, "bf16"),
+                                          (1, 1, 16, 128, "f32"), (3, 64, 528, 1024, "bf16")])
+def test_nvfp4_scaled_matmul(Bt, M, N, K, out):
+    torch = _torch()
+    say("nvfp4", Bt, M, N, K, out)
+    a = synth.random_e2m1_codes((Bt, M, K), 900 + M)
+    b = synth.random_e2m1_codes((Bt, N, K), 901 + M)
+    sa = synth.random_e4m3_scale_codes((Bt, M, K // 16), 902 + M, 1, 14)
+    sb = synth.random_e4m3_scale_codes((Bt, N, K // 16), 903 + M, 1, 14)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y, ws = _run_nvfp4(a, b, sa, sb, od)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, OF.E2M1, OF.E2M1, OF.E4M3)
+    yh = host(y) if out == "f32" else OF.decode_bf16(host(y))
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
+    # the dequantized lhs in the workspace: exactly value x scale in bf16
+    wa = host(ws)[:Bt * M * K * 2].view(np.uint16).reshape(Bt, M, K)
+    exact = OF.decode_e2m1(a) * np.repeat(OF.decode(sa, OF.E4M3), 16, axis=-1)
+    assert_bytes_equal(wa, OF.encode_bf16(exact.astype(np.float32)), "dequantized lhs")
+    assert np.array_equal(OF.decode_bf16(wa), exact)
+
+
+def test_nvfp4_full_size_sampled():
+    """m = n = k = 4096 nvfp4: sampled rows."""
+    torch = _torch()
+    Bt, M, N, K = 1, 4096, 4096, 4096
+    say("nvfp4 full size", M, N, K)
+    a = synth.random_e2m1_codes((Bt, M, K), 910)
+    b = synth.random_e2m1_codes((Bt, N, K), 911)
+    sa = synth.random_e4m3_scale_codes((Bt, M, K // 16), 912)
+    sb = synth.random_e4m3_scale_codes((Bt, N, K // 16), 913)
+    y, _ = _run_nvfp4(a, b, sa, sb, torch.float32)
+    y = host(y)
+    rows = _rows_sample(M, seed=9)
+    yr, T = OM.scaled_matmul(a[:, rows], b, sa[:, rows], sb, OF.E2M1, OF.E2M1, OF.E4M3)
+    assert_within_T(y[:, rows], yr, T, "y rows")
+    assert np.all(np.isfinite(y)), "unwritten output"
+
+
 # ---------------------------------------------------------------- MX -------
 
 def _mx_scaled_abs(codes, scales, fmt):
