@@ -553,20 +553,29 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
 
 // ---------------------------------------------------------------------------
 // Small and skinny products (few 256 x 256 tiles): split K inside the
-// workgroup.  SKW waves share one 64 x 64 output tile; wave w runs K-steps
-// [w * per, (w + 1) * per) over the whole tile, loading its own fragments
-// straight from global memory into registers (nothing is shared, so the
-// K loop has no barrier), next step's fragments in flight while the current
-// step is multiplied.  The SKW partial tiles then meet in LDS and each
-// output is the sum of the partials in wave order - the result does not
-// depend on timing.  Same MFMAs, scales and epilogue as k_gemm.
+// workgroup.  SKW waves (4 or 8) share one 64 x 64 output tile; wave w runs
+// K-steps [w * per, (w + 1) * per) over the whole tile.  Each wave stages
+// its own A and B tiles of a step (16 KiB) in a private LDS region with the
+// big kernel's direct loads (8 rows x 128 bytes per instruction: whole cache
+// lines; loading MFMA fragments straight into registers reads 64-byte half
+// lines of 16 rows per instruction, and ran at a third of the rate) and
+// swizzle; nothing is shared, so the K loop has no barrier.  Once a step's
+// fragments are in registers the region takes the next step's tiles, which
+// are in flight while the step is multiplied.  One region per wave (not
+// two) keeps a 4-wave workgroup at 64 KiB of LDS, two per CU; a long K over
+// fewer tiles than that fills takes 8 waves per workgroup.  The SKW
+// partial tiles then meet in LDS (the stage area) and each output is the
+// sum of the partials in wave order - the result does not depend on timing.
+// Same MFMAs, scales and epilogue as k_gemm.
 constexpr int SK_T = 64;  // output tile edge
-constexpr int SKW = 4;    // waves (K slices) per workgroup
 
-template <int MODE, int OUT_BF16, int FA, int FB>
-__global__ void __launch_bounds__(64 * SKW, 1) k_gemm_sk(GemmArgs p) {
+template <int MODE, int OUT_BF16, int FA, int FB, int SKW>
+__global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
   typedef typename std::conditional<MODE == MODE_I8, v4i, v4f>::type acc_t;
-  __shared__ __attribute__((aligned(16))) acc_t red[SKW][SK_T * SK_T / 4];
+  constexpr int kStage = 2 * SK_T * BK;  // A then B tile of one K-step
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sk[SKW * kStage];
+  static_assert(sizeof(acc_t) * SKW * SK_T * SK_T / 4 <= sizeof(lds_sk), "partials fit the stage area");
+  acc_t (*red)[SK_T * SK_T / 4] = reinterpret_cast<acc_t (*)[SK_T * SK_T / 4]>(lds_sk);
 
   const int tid = threadIdx.x;
   const int batch = blockIdx.z;
@@ -580,24 +589,41 @@ __global__ void __launch_bounds__(64 * SKW, 1) k_gemm_sk(GemmArgs p) {
 
   const uint8_t* A = p.A + int64_t(batch) * p.sA;
   const uint8_t* B = p.B + int64_t(batch) * p.sB;
-  const int64_t a_bytes = int64_t(M) * K, b_bytes = int64_t(N) * K;
-  // lane offset inside a 16-row block: row r16, bytes 16 g (and +64)
-  const int voff = r16 * K + 16 * g;
-
-  // fragments of one K-step: f[0..3] A blocks (rows 16 i), f[4..7] B blocks
-  auto load_step = [&](int ks, v8i (&f)[8]) {
+  // this wave's LDS stages: stage st at + st * kStage, A rows then B rows
+  uint8_t* const my = lds_sk + w * kStage;
+  // direct loads: lane i of an 8-row slice fills LDS bytes [16 i, 16 i + 16)
+  // of it, i.e. row i / 8, physical chunk i % 8, which holds the logical
+  // chunk (i % 8) ^ (row & 7); rows at or past M (N) read as zero
+  const int lrow = lane >> 3;
+  const int voff = lrow * K + 16 * ((lane & 7) ^ lrow);
+  int a_rec[8], b_rec[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint8_t* base = b < 4 ? A : B;
-      const int row0 = (b < 4 ? m0 : n0) + 16 * (b & 3);
-      const int64_t off = int64_t(row0) * K + int64_t(ks) * BK;
-      const int64_t rec = (b < 4 ? a_bytes : b_bytes) - off;
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(base + off), (short)0,
-          int(rec < 0 ? 0 : (rec > 0x7FFFFFFF ? 0x7FFFFFFF : rec)), 0x00020000);
-      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
-      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 64, 0, 0);
-      f[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  for (int sl = 0; sl < 8; ++sl) {
+    a_rec[sl] = max(0, min(M - (m0 + 8 * sl), 8)) * K;
+    b_rec[sl] = max(0, min(N - (n0 + 8 * sl), 8)) * K;
+  }
+  const uint32_t my_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(my));
+  auto dma_step = [&](int ks, int st) {
+    const int kb = ks * BK;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) {
+      lds_dma16(rsrc32(A + int64_t(m0 + 8 * sl) * K + kb, max(a_rec[sl] - kb, 0)), voff,
+                my_addr + uint32_t(st * kStage + sl * 8 * BK));
+      lds_dma16(rsrc32(B + int64_t(n0 + 8 * sl) * K + kb, max(b_rec[sl] - kb, 0)), voff,
+                my_addr + uint32_t(st * kStage + SK_T * BK + sl * 8 * BK));
+    }
+  };
+  // fragment reads: row r's logical chunk c sits at physical chunk c ^ (r & 7)
+  const int swz = r16 & 7;
+  const int c0 = 16 * (g ^ swz), c1 = 16 * ((g + 4) ^ swz);
+  auto load_step = [&](int st, v8i (&f)[8]) {
+    const uint8_t* ta = my + st * kStage;
+    const uint8_t* tb = ta + SK_T * BK;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = 16 * b + r16;
+      f[b] = lds_frag(ta, row * BK + c0, row * BK + c1);
+      f[4 + b] = lds_frag(tb, row * BK + c0, row * BK + c1);
     }
   };
   // per-step scales of this lane: A rows 16 i + r16, B rows (MX) or group
@@ -627,14 +653,19 @@ __global__ void __launch_bounds__(64 * SKW, 1) k_gemm_sk(GemmArgs p) {
     for (int i = 0; i < 4; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
 
   if (k_begin < k_end) {
-    v8i cur[8], nxt[8];
+    v8i cur[8];
     float sa[4], sb = 0.f, na[4], nb = 0.f;
     int qa[4], qb[4], nqa[4], nqb[4];
-    load_step(k_begin, cur);
+    dma_step(k_begin, 0);
     load_scales(k_begin, sa, sb, qa, qb);
     for (int ks = k_begin; ks < k_end; ++ks) {
-      const int kn = min(ks + 1, k_end - 1);  // the last step re-reads itself: no branch
-      load_step(kn, nxt);
+      // this step's tiles and scales have landed; once its fragments are in
+      // registers the stage takes the next step's tiles
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      load_step(0, cur);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int kn = min(ks + 1, k_end - 1);  // the last step reloads itself: no branch
+      dma_step(kn, 0);
       load_scales(kn, na, nb, nqa, nqb);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -660,8 +691,6 @@ __global__ void __launch_bounds__(64 * SKW, 1) k_gemm_sk(GemmArgs p) {
         }
       }
 #pragma unroll
-      for (int b = 0; b < 8; ++b) cur[b] = nxt[b];
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
         sa[i] = na[i];
         qa[i] = nqa[i];
@@ -671,9 +700,12 @@ __global__ void __launch_bounds__(64 * SKW, 1) k_gemm_sk(GemmArgs p) {
     }
   }
 
-  // ---- the partial tiles meet in LDS: element (row, col) of wave w's
-  // partial at red[w][(row * 64 + col) / 4]; lane holds rows 16 i + r16,
-  // columns 16 j + 4 g .. + 3
+  // ---- the partial tiles meet in LDS (over the stage area, once every
+  // wave is done with it and its last loads have landed): element (row,
+  // col) of wave w's partial at red[w][(row * 64 + col) / 4]; lane holds
+  // rows 16 i + r16, columns 16 j + 4 g .. + 3
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -757,7 +789,14 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   if constexpr (MODE != MODE_BF16) {
     if (tiles < kSkinnyTiles && !GN1) {
       dim3 grid(unsigned((a.N + SK_T - 1) / SK_T), unsigned((a.M + SK_T - 1) / SK_T), unsigned(batch));
-      hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB>), grid, 64 * SKW, 0, st, a);
+      // 4 waves (64 KiB, two workgroups per CU); 8 waves (K split finer,
+      // one workgroup per CU) only for a long K over too few tiles to fill
+      // two per CU - measured faster there and slower elsewhere
+      const int64_t sk_tiles = int64_t(grid.x) * grid.y * grid.z;
+      if (sk_tiles >= 512 || a.K / BK < 64)
+        hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB, 4>), grid, 256, 0, st, a);
+      else
+        hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB, 8>), grid, 512, 0, st, a);
       return launch_status("gemm (split K)");
     }
   }

@@ -97,8 +97,11 @@ def test_blockwise_small_end_to_end():
 
 @pytest.mark.parametrize("M,N,K", [
     (237, 4096, 4096), (349, 2048, 2048), (1, 128, 128), (300, 384, 640), (513, 256, 256),
+    (1024, 2048, 2048), (130, 1024, 8192),
 ])
 def test_blockwise_full_compare(M, N, K):
+    """Recipe operands against the oracle; the small products run the
+    split-K kernel (4 waves; 8 waves for 130 x 1024 x 8192)."""
     say("blockwise full (recipe operands)", M, N, K)
     a, b, sa, sb = _recipe_blockwise(M, N, K, 600 + M)
     y = _run_blockwise(a, b, sa, sb)
