@@ -8,10 +8,15 @@
 // within an ulp of x / s, the residual x - q0 * s is exact in one FMA, and
 // q0 + (x - q0 * s) * r rounds to the correctly rounded quotient whenever
 // nothing underflows (Markstein's theorem on division by a correctly
-// rounded reciprocal).  Quotients below 2^-11 - where underflow can occur -
-// only ever encode to a zero of x's sign, and are returned as that zero.
-// float32 -> fp8 uses the gfx950 conversion instructions (nearest, ties to
-// even; inputs already clamped to the format's range).
+// rounded reciprocal).  Where the residual underflows (|x| below about
+// 2^-102) the quotient is below 2^-60 and still encodes to a zero; the sign
+// of a zero quotient is taken from x.  The per-block scale amax / 448 and
+// its reciprocal are formed the same way without a division instruction
+// sequence (see scale_e4m3 and recip).  float32 -> fp8 uses the gfx950
+// conversion instructions (nearest, ties to even; inputs already clamped to
+// the format's range).  Block maxima are taken on the bits of |x| (for
+// finite values their unsigned order is the order of |x|) with DPP and
+// permlane lane exchanges, which stay in the VALU.
 #include "common.h"
 #include "quant.h"
 
@@ -22,20 +27,61 @@ namespace {
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE5M2Max = 57344.0f;
 
-__device__ __forceinline__ float amax4(float4 v) {
-  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+// |x| as bits: for finite x the unsigned order of these is the order of |x|.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+__device__ __forceinline__ uint32_t amax4_bits(float4 v) {
+  return max(max(abs_bits(v.x), abs_bits(v.y)), max(abs_bits(v.z), abs_bits(v.w)));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over aligned groups of WIDTH lanes (2 .. 64), left in every lane of
+// the group.  Quad permutations give the maximum of each 4 lanes; mirroring
+// each half row (lane i <-> 7 - i) then each row (i <-> 15 - i) pairs every
+// 4- then 8-lane group with its neighbour; v_permlane16_swap exchanges rows
+// 0 <-> 1 and 2 <-> 3, v_permlane32_swap the two halves of the wave.
 template <int WIDTH>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = WIDTH / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WIDTH));
+__device__ __forceinline__ uint32_t group_max_bits(uint32_t v) {
+  static_assert(WIDTH >= 2 && WIDTH <= 64 && (WIDTH & (WIDTH - 1)) == 0, "group width");
+  v = max(v, dpp_mov<0xB1>(v));  // quad_perm [1, 0, 3, 2]
+  if constexpr (WIDTH >= 4) v = max(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  if constexpr (WIDTH >= 8) v = max(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if constexpr (WIDTH >= 16) v = max(v, dpp_mov<0x140>(v));  // row_mirror
+  if constexpr (WIDTH >= 32) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(uint32_t(p[0]), uint32_t(p[1]));
+  }
+  if constexpr (WIDTH >= 64) {
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = max(uint32_t(p[0]), uint32_t(p[1]));
+  }
   return v;
 }
 
-// fp32 block scale of the block_scaled_mm recipe: max(amax / 448, 1e-10).
+// fp32 block scale of the block_scaled_mm recipe: max(amax / 448, 1e-10),
+// the quotient correctly rounded.  Markstein's form with the correctly
+// rounded constant 1/448: q0 = amax * (1/448) is within an ulp, the residual
+// amax - 448 q0 is exact in one FMA, and the corrected quotient is the
+// correctly rounded amax / 448 (no underflow matters: below 448e-10 the
+// floor is taken).  Checked bit for bit against IEEE division on every
+// float32 amax from 2^-40 to the largest float.
 __device__ __forceinline__ float fp8_block_scale(float amax) {
-  return fmaxf(amax / kE4M3Max, scale_floor());
+  constexpr float kInv = 1.0f / kE4M3Max;
+  const float q0 = amax * kInv;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, kE4M3Max, amax), kInv, q0);
+  return fmaxf(q, scale_floor());
+}
+
+// 1 / s correctly rounded for the scales above (normal, 1e-10 <= s < 2^120):
+// the hardware reciprocal (within an ulp) and one Newton step whose
+// residual 1 - s y0 is exact in the FMA.  Checked bit for bit against IEEE
+// division on every float32 s in that range.
+__device__ __forceinline__ float recip(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  return __builtin_fmaf(__builtin_fmaf(-s, y0, 1.0f), y0, y0);
 }
 
 // Four float32 in [-fmax, fmax] to four fp8 codes (first value in the low
@@ -49,16 +95,16 @@ __device__ __forceinline__ uint32_t cvt4_e5m2(float a, float b, float c, float d
   return uint32_t(__builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true));
 }
 
-// x / s correctly rounded for |x / s| >= 2^-11, a zero of x's sign below
-// (r = 1 / s correctly rounded, s > 0 normal).
+// x / s correctly rounded (r = 1 / s correctly rounded, s > 0 normal); a
+// zero quotient carries x's sign (-0 / s is -0).
 __device__ __forceinline__ float quot(float x, float s, float r) {
   const float q0 = x * r;
   const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, s, x), r, q0);
-  return fabsf(q0) < 0x1p-11f ? __builtin_copysignf(0.0f, x) : q1;
+  return __builtin_copysignf(q1, x);
 }
 
 __device__ __forceinline__ uint32_t quant4_e4m3(float4 v, float s, float r) {
-  auto q = [s, r](float x) { return fminf(fmaxf(quot(x, s, r), -kE4M3Max), kE4M3Max); };
+  auto q = [s, r](float x) { return __builtin_amdgcn_fmed3f(quot(x, s, r), -kE4M3Max, kE4M3Max); };
   return cvt4_e4m3(q(v.x), q(v.y), q(v.z), q(v.w));
 }
 
@@ -81,9 +127,9 @@ __global__ void __launch_bounds__(256) k_fp8_rowblock(const float4* __restrict__
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t f = base + u * 256 + threadIdx.x;
-      const float amax = group_max<LPB>(amax4(v[u]));
+      const float amax = __uint_as_float(group_max_bits<LPB>(amax4_bits(v[u])));
       const float s = fp8_block_scale(amax);
-      const float r = 1.0f / s;
+      const float r = recip(s);
       if (f < n4) {
         codes[f] = quant4_e4m3(v[u], s, r);
         if ((threadIdx.x % LPB) == 0) scales[f / LPB] = s;
@@ -98,26 +144,26 @@ __global__ void __launch_bounds__(256) k_fp8_rowblock(const float4* __restrict__
 __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ src,
                                                      uint8_t* __restrict__ codes,
                                                      float* __restrict__ scales, int64_t cols) {
-  __shared__ float wmax[4];
+  __shared__ uint32_t wmax[4];
   const int tx = threadIdx.x;
   const int c4 = tx & 31;
   const int r0 = tx >> 5;
   const int64_t row0 = int64_t(blockIdx.y) * 128;
   const int64_t col0 = int64_t(blockIdx.x) * 128 + 4 * c4;
   float4 v[16];
-  float m = 0.f;
+  uint32_t m = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const float4* p = reinterpret_cast<const float4*>(src + (row0 + r0 + 8 * i) * cols + col0);
     v[i] = ldnt(p);
-    m = fmaxf(m, amax4(v[i]));
+    m = max(m, amax4_bits(v[i]));
   }
-  m = group_max<64>(m);
+  m = group_max_bits<64>(m);
   if ((tx & 63) == 0) wmax[tx >> 6] = m;
   __syncthreads();
-  const float amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float amax = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
   const float s = fp8_block_scale(amax);
-  const float r = 1.0f / s;
+  const float r = recip(s);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     uint32_t* q = reinterpret_cast<uint32_t*>(codes + (row0 + r0 + 8 * i) * cols + col0);
@@ -144,7 +190,7 @@ __device__ __forceinline__ uint32_t mx_encode4(const float* x, int E) {
   constexpr float fmax = CODE == 0 ? kE4M3Max : kE5M2Max;
   float y[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) y[i] = fminf(fmaxf(ldexpf(x[i], -E), -fmax), fmax);
+  for (int i = 0; i < 4; ++i) y[i] = __builtin_amdgcn_fmed3f(ldexpf(x[i], -E), -fmax, fmax);
   return CODE == 0 ? cvt4_e4m3(y[0], y[1], y[2], y[3]) : cvt4_e5m2(y[0], y[1], y[2], y[3]);
 }
 
@@ -191,11 +237,10 @@ __global__ void __launch_bounds__(256) k_mx_rows(const void* __restrict__ src,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t f = base + u * 256 + threadIdx.x;
-      float m = 0.f;
+      uint32_t m = 0u;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[u][i]));
-      m = group_max<4>(m);
-      const int E = mx_exponent<EMAX>(m);
+      for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[u][i]));
+      const int E = mx_exponent<EMAX>(__uint_as_float(group_max_bits<4>(m)));
       if (f < n8) {
         codes[f] = make_uint2(mx_encode4<CODE>(&x[u][0], E), mx_encode4<CODE>(&x[u][4], E));
         if ((threadIdx.x & 3) == 0) scales[f >> 2] = uint8_t(E + 127);
@@ -235,14 +280,13 @@ __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
   __syncthreads();
   const int oc = tx >> 2, seg = tx & 3;
   float x[16];
-  float m = 0.f;
+  uint32_t m = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     x[i] = tile[16 * seg + i][oc];
-    m = fmaxf(m, fabsf(x[i]));
+    m = max(m, abs_bits(x[i]));
   }
-  m = fmaxf(m, __shfl_xor(m, 1, 64));
-  const int E = mx_exponent<EMAX>(m);
+  const int E = mx_exponent<EMAX>(__uint_as_float(group_max_bits<2>(m)));
   const int64_t orow = c0 + oc;
   const int64_t ocol = r0 + 16 * seg;
   if (orow < cols && ocol < rows) {
@@ -275,17 +319,18 @@ __device__ __forceinline__ uint32_t int8_pack4(float4 v, float s, float r) {
          ((uint32_t(int8_code(v.z, s, r)) & 0xFFu) << 16) | ((uint32_t(int8_code(v.w, s, r)) & 0xFFu) << 24);
 }
 
+// Maximum of |x| bits over the workgroup's N waves, as a float.
 template <int N>
-__device__ __forceinline__ float block_max(float m, float* red) {
-  m = group_max<64>(m);
+__device__ __forceinline__ float block_max(uint32_t m, uint32_t* red) {
+  m = group_max_bits<64>(m);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = m;
   __syncthreads();
-  float r = red[0];
+  uint32_t r = red[0];
 #pragma unroll
-  for (int i = 1; i < N; ++i) r = fmaxf(r, red[i]);
-  return r;
+  for (int i = 1; i < N; ++i) r = max(r, red[i]);
+  return __uint_as_float(r);
 }
 
 // One workgroup per row, D % 4 == 0, the row held in registers (V float4
@@ -294,16 +339,16 @@ template <int V>
 __global__ void __launch_bounds__(256) k_int8_rows_vec(const float* __restrict__ x,
                                                        uint32_t* __restrict__ xq,
                                                        float* __restrict__ xs, int64_t D) {
-  __shared__ float red[4];
+  __shared__ uint32_t red[4];
   const int64_t d4 = D / 4;
   const float4* row = reinterpret_cast<const float4*>(x + int64_t(blockIdx.x) * D);
   float4 v[V];
-  float m = 0.f;
+  uint32_t m = 0u;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     const int64_t c = threadIdx.x + 256 * i;
     v[i] = c < d4 ? ldnt(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    m = fmaxf(m, amax4(v[i]));
+    m = max(m, amax4_bits(v[i]));
   }
   const float s = int8_scale(block_max<4>(m, red));
   const float r = 1.0f / s;
@@ -320,10 +365,10 @@ __global__ void __launch_bounds__(256) k_int8_rows_vec(const float* __restrict__
 __global__ void __launch_bounds__(256) k_int8_rows_any(const float* __restrict__ x,
                                                        int8_t* __restrict__ xq,
                                                        float* __restrict__ xs, int64_t D) {
-  __shared__ float red[4];
+  __shared__ uint32_t red[4];
   const float* row = x + int64_t(blockIdx.x) * D;
-  float m = 0.f;
-  for (int64_t c = threadIdx.x; c < D; c += 256) m = fmaxf(m, fabsf(row[c]));
+  uint32_t m = 0u;
+  for (int64_t c = threadIdx.x; c < D; c += 256) m = max(m, abs_bits(row[c]));
   const float s = int8_scale(block_max<4>(m, red));
   const float r = 1.0f / s;
   int8_t* out = xq + int64_t(blockIdx.x) * D;

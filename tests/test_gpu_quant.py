@@ -56,6 +56,31 @@ def test_fp8_rowblock(shape, group):
     assert_bytes_equal(host(c), rc, "codes")
 
 
+def test_fp8_rowblock_scales_over_all_binades():
+    """Every 1x128 block gets its own magnitude, 2^e (1 + f) with e from -45
+    to 110 and f uniform: the block scales (amax / 448, correctly rounded,
+    floored at 1e-10) and their reciprocals then cover every binade the
+    recipe can produce, each compared bit for bit with the oracle through
+    the scales and through the codes they make."""
+    torch = _torch()
+    rows, cols = 2048, 4096
+    say("fp8_rowblock binades", rows, cols)
+    x = synth.randn_f32((rows, cols), 404)
+    rng = np.random.default_rng(405)
+    nb = cols // 128
+    e = rng.integers(-45, 111, size=(rows, nb))
+    f = rng.random((rows, nb))
+    mag = (np.ldexp(1.0 + f, e)).astype(np.float32)
+    x = (x.reshape(rows, nb, 128) * mag[:, :, None]).reshape(rows, cols).astype(np.float32)
+    assert np.all(np.isfinite(x))
+    c = empty((rows, cols), torch.uint8)
+    s = empty((rows, nb), torch.float32)
+    bsq.bsq_quant_fp8_rowblock(to_dev(x), c, s, 128)
+    rc, rs = OQ.fp8_rowblock(x, 128)
+    assert_bytes_equal(host(s).view(np.uint32), rs.view(np.uint32), "scales")
+    assert_bytes_equal(host(c), rc, "codes")
+
+
 @pytest.mark.parametrize("shape", [(512, 512), (4096, 4096), (128, 384)])
 def test_fp8_tile(shape):
     torch = _torch()
