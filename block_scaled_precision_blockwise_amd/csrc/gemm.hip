@@ -267,9 +267,10 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   // bytes), i.e. row (slice_row0 + i / 8), physical chunk i % 8; it fetches
   // the logical chunk that the XOR swizzle stores there.  Wave w moves
   // slices w, w + NW, ... of A and of B per K-step.  One descriptor per
-  // slice (scalar registers) starts at that slice's first row and K-step;
-  // rows at or past M (N) fall outside its range and read as zero, so
-  // tails need no clamping.
+  // slice (scalar registers), built once: it starts at the slice's first
+  // row and covers its rows inside the operand, so rows at or past M (N)
+  // fall outside its range and read as zero and tails need no clamping.
+  // A K-step only moves the lane offset, which all slices share.
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lrow = 8 * w + (lane >> 3);
   const int llog = (lane & 7) ^ (lrow & 7);
@@ -283,15 +284,18 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     a_rec[s] = max(0, min(M - (m0 + 8 * NW * s), 8 * NW)) * K;
     b_rec[s] = max(0, min(N - (n0 + 8 * NW * s), 8 * NW)) * K;
   }
+  i32x4 ra[SPW], rb[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    if (s < SPWA) ra[s] = rsrc32(A + int64_t(m0 + 8 * NW * s) * K, a_rec[s]);
+    rb[s] = rsrc32(B + int64_t(n0 + 8 * NW * s) * K, b_rec[s]);
+  }
   const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_a + 8 * w * BK));
   const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_b + 8 * w * BK));
   auto gload_slice = [&](int ks, int st, int s) {
-    const int kb = ks * BK;
-    if (s < SPWA)
-      lds_dma16(rsrc32(A + int64_t(m0 + 8 * NW * s) * K + kb, max(a_rec[s] - kb, 0)), voff,
-                la_base + uint32_t(st * TBM * BK + 8 * NW * s * BK));
-    lds_dma16(rsrc32(B + int64_t(n0 + 8 * NW * s) * K + kb, max(b_rec[s] - kb, 0)), voff,
-              lb_base + uint32_t(st * BN * BK + 8 * NW * s * BK));
+    const int vk = voff + ks * BK;  // < 8 NW K
+    if (s < SPWA) lds_dma16(ra[s], vk, la_base + uint32_t(st * TBM * BK + 8 * NW * s * BK));
+    lds_dma16(rb[s], vk, lb_base + uint32_t(st * BN * BK + 8 * NW * s * BK));
   };
   auto gload = [&](int ks, int st) {
 #pragma unroll
@@ -593,24 +597,20 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
   uint8_t* const my = lds_sk + w * kStage;
   // direct loads: lane i of an 8-row slice fills LDS bytes [16 i, 16 i + 16)
   // of it, i.e. row i / 8, physical chunk i % 8, which holds the logical
-  // chunk (i % 8) ^ (row & 7); rows at or past M (N) read as zero
+  // chunk (i % 8) ^ (row & 7).  One descriptor per operand, built once,
+  // covers the tile's rows inside the operand (rows at or past M (N) read
+  // as zero); slice and K-step only move the lane offset (< 64 K).
   const int lrow = lane >> 3;
   const int voff = lrow * K + 16 * ((lane & 7) ^ lrow);
-  int a_rec[8], b_rec[8];
-#pragma unroll
-  for (int sl = 0; sl < 8; ++sl) {
-    a_rec[sl] = max(0, min(M - (m0 + 8 * sl), 8)) * K;
-    b_rec[sl] = max(0, min(N - (n0 + 8 * sl), 8)) * K;
-  }
+  const i32x4 ra = rsrc32(A + int64_t(m0) * K, max(0, min(M - m0, SK_T)) * K);
+  const i32x4 rb = rsrc32(B + int64_t(n0) * K, max(0, min(N - n0, SK_T)) * K);
   const uint32_t my_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(my));
   auto dma_step = [&](int ks, int st) {
-    const int kb = ks * BK;
+    const int vk = voff + ks * BK;
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      lds_dma16(rsrc32(A + int64_t(m0 + 8 * sl) * K + kb, max(a_rec[sl] - kb, 0)), voff,
-                my_addr + uint32_t(st * kStage + sl * 8 * BK));
-      lds_dma16(rsrc32(B + int64_t(n0 + 8 * sl) * K + kb, max(b_rec[sl] - kb, 0)), voff,
-                my_addr + uint32_t(st * kStage + SK_T * BK + sl * 8 * BK));
+      lds_dma16(ra, vk + 8 * sl * K, my_addr + uint32_t(st * kStage + sl * 8 * BK));
+      lds_dma16(rb, vk + 8 * sl * K, my_addr + uint32_t(st * kStage + SK_T * BK + sl * 8 * BK));
     }
   };
   // fragment reads: row r's logical chunk c sits at physical chunk c ^ (r & 7)
