@@ -91,37 +91,34 @@ def _hip_runtime():
 
 
 class KernelTimer:
-    """HIP events around individual launches, recorded on the stream the
-    kernel is launched on (torch's current stream, which the binding passes
-    to the library).  The events are created with hipEventDisableSystemFence:
-    a timing-only event then skips the system-scope cache writeback and
-    invalidation that a default event performs, which would otherwise be
-    charged to - and slow - the kernel it brackets.  Each pair still
-    includes the dispatch gap that its start marker opens before the kernel
-    (about 5 us here; the kernel trace shows it)."""
-
-    FLAGS = 0x20000000  # hipEventDisableSystemFence (timing stays enabled)
+    """Per-launch HIP events for the GEMM kernel, recorded by the kernel's
+    own dispatch: before each timed GEMM call the library is asked
+    (bsq_time_next_gemm) to launch its next GEMM kernel with
+    hipExtLaunchKernel and these two events, which then hold that kernel's
+    start and end on the stream it runs on.  No marker packet sits between
+    the kernels, so the step keeps its back-to-back schedule and the pair
+    measures the kernel alone (a separate hipEventRecord before the kernel
+    would also count the dispatch gap that its marker opens, ~5 us)."""
 
     def __init__(self, torch, launches):
         import ctypes
         self.ct = ctypes
         self.hip = _hip_runtime()
-        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.events = []
         for _ in range(2 * launches):
             ev = ctypes.c_void_p()
-            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.FLAGS)
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), 0)
             if rc != 0:
                 raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             self.events.append(ev)
         self.used = 0
 
     def around(self, fn):
+        import block_scaled_precision_blockwise_amd as bsq
         s, e = self.events[self.used], self.events[self.used + 1]
         self.used += 2
-        self.hip.hipEventRecord(s, self.stream)
+        bsq.bsq_time_next_gemm(s.value, e.value)
         fn()
-        self.hip.hipEventRecord(e, self.stream)
 
     def mean_ms(self):
         total = 0.0

@@ -25,7 +25,7 @@ from typing import Optional
 __all__ = [
     "BSQ_F32", "BSQ_BF16", "BSQ_E4M3", "BSQ_E5M2", "BSQ_E8M0", "BSQ_I8", "BSQ_I32",
     "lib", "lib_path", "is_built",
-    "bsq_version", "bsq_device_check",
+    "bsq_version", "bsq_device_check", "bsq_time_next_gemm",
     "bsq_quant_fp8_rowblock", "bsq_quant_fp8_tile", "bsq_quant_mx",
     "bsq_int8_quant_rows", "bsq_int8_quant_cols",
     "bsq_blockwise_fp8_matmul", "bsq_scaled_matmul", "bsq_int8_matmul",
@@ -52,6 +52,7 @@ _SIGNATURES = {
     "bsq_status_string": (ctypes.c_char_p, [_INT]),
     "bsq_last_error": (ctypes.c_char_p, []),
     "bsq_device_check": (_INT, []),
+    "bsq_time_next_gemm": (_INT, [_P, _P]),
     "bsq_quant_fp8_rowblock": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P]),
     "bsq_quant_fp8_tile": (_INT, [_I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     "bsq_quant_mx": (_INT, [_I64, _I64, _INT, _P, _INT, _P, _INT, _P, _P]),
@@ -179,6 +180,12 @@ def bsq_version() -> str:
 
 def bsq_device_check() -> None:
     _raise(lib().bsq_device_check(), "bsq_device_check")
+
+
+def bsq_time_next_gemm(start_event: Optional[int], stop_event: Optional[int]) -> None:
+    """The next GEMM kernel launched by this thread records these HIP events
+    (raw hipEvent_t handles, or None) at its own start and end."""
+    _raise(lib().bsq_time_next_gemm(start_event, stop_event), "bsq_time_next_gemm")
 
 
 def bsq_quant_fp8_rowblock(src, codes, scales, group: int = 128, stream=None):

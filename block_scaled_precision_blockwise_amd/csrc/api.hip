@@ -14,6 +14,7 @@ namespace bsq {
 
 namespace {
 thread_local std::string g_last_error;
+thread_local GemmEvents g_gemm_events;
 std::mutex g_dev_mu;
 std::vector<int> g_dev_state;  // per device: 0 unknown, 1 gfx950, 2 other
 }  // namespace
@@ -26,6 +27,12 @@ bsq_status fail(bsq_status st, const std::string& msg) {
 bsq_status ok() {
   g_last_error.clear();
   return BSQ_OK;
+}
+
+GemmEvents take_gemm_events() {
+  const GemmEvents e = g_gemm_events;
+  g_gemm_events = GemmEvents{};
+  return e;
 }
 
 bsq_status require_gfx950() {
@@ -98,6 +105,12 @@ const char* bsq_last_error(void) { return g_last_error.c_str(); }
 bsq_status bsq_device_check(void) {
   const bsq_status s = require_gfx950();
   return s == BSQ_OK ? ok() : s;
+}
+
+bsq_status bsq_time_next_gemm(void* start_event, void* stop_event) {
+  g_gemm_events.start = static_cast<hipEvent_t>(start_event);
+  g_gemm_events.stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
 }
 
 // ------------------------------------------------------------ quantizers --

@@ -20,6 +20,14 @@ bsq_status require_gfx950();
 // Maps the result of a kernel launch to a status.
 bsq_status launch_status(const char* what);
 
+// Events that the next GEMM kernel launched on this thread records at its
+// start and end (set by bsq_time_next_gemm); taking them clears them.
+struct GemmEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+GemmEvents take_gemm_events();
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 #define BSQ_CHECK_PTR(p)                                                     \

@@ -25,6 +25,8 @@
 // The result lane l holds column l % 16 of rows 4*(l/16) .. +3.  The MFMA's
 // first operand is the B fragment, so a lane's four results are four
 // consecutive n of one m: one 16-byte store, one A scale per lane.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -777,13 +779,25 @@ constexpr int64_t kHalfTiles = 134;
 // (the big-tile kernel would leave most of the 256 CUs idle).
 constexpr int64_t kSkinnyTiles = 64;
 
+// Launches a GEMM kernel; when the caller asked for timing events
+// (bsq_time_next_gemm), through hipExtLaunchKernel so that the events
+// record this kernel's own start and end.
+template <typename Kernel, typename... Args>
+void launch_gemm_kernel(Kernel k, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  const GemmEvents ev = take_gemm_events();
+  if (ev.start != nullptr || ev.stop != nullptr)
+    hipExtLaunchKernelGGL(k, grid, block, 0, st, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(k, grid, block, 0, st, args...);
+}
+
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int GEN = 0>
 bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   const int64_t tiles = int64_t((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * batch;
   if constexpr (GEN != 0) {
     // general scale blocks: the big-tile kernel at every size
     dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
-    hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1>), grid, 512, 0, st, a);
+    launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1>, grid, dim3(512), st, a);
     return launch_status("gemm (general scale blocks)");
   }
   if constexpr (MODE != MODE_BF16) {
@@ -794,9 +808,9 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
       // two per CU - measured faster there and slower elsewhere
       const int64_t sk_tiles = int64_t(grid.x) * grid.y * grid.z;
       if (sk_tiles >= 512 || a.K / BK < 64)
-        hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB, 4>), grid, 256, 0, st, a);
+        launch_gemm_kernel(k_gemm_sk<MODE, OUT_BF16, FA, FB, 4>, grid, dim3(256), st, a);
       else
-        hipLaunchKernelGGL((k_gemm_sk<MODE, OUT_BF16, FA, FB, 8>), grid, 512, 0, st, a);
+        launch_gemm_kernel(k_gemm_sk<MODE, OUT_BF16, FA, FB, 8>, grid, dim3(512), st, a);
       return launch_status("gemm (split K)");
     }
   }
@@ -804,10 +818,10 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   if (tiles <= kHalfTiles) {
     // doubling the tile count still fits one pass over the CUs: 128-row tiles
     dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + 127) / 128), unsigned(batch));
-    hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 128>), grid, 64 * NW, 0, st, a);
+    launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 128>, grid, dim3(64 * NW), st, a);
   } else {
     dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
-    hipLaunchKernelGGL((k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 256>), grid, 64 * NW, 0, st, a);
+    launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 256>, grid, dim3(64 * NW), st, a);
   }
   return launch_status("gemm");
 }
@@ -836,8 +850,8 @@ bsq_status launch_int8_matmul_small(int64_t B, int64_t D_in, int64_t D_out, cons
                                     int32_t* acc, hipStream_t st) {
   const int64_t n = B * D_out;
   if (n == 0) return ok();
-  hipLaunchKernelGGL(k_int8_small, unsigned((n + 255) / 256), 256, 0, st, xq, wqT, xs, ws, y, acc,
-                     B, D_in, D_out);
+  launch_gemm_kernel(k_int8_small, dim3(unsigned((n + 255) / 256)), dim3(256), st, xq, wqT, xs, ws, y,
+                     acc, B, D_in, D_out);
   return launch_status("int8_matmul (small shapes)");
 }
 

@@ -72,6 +72,15 @@ const char* bsq_last_error(void);
 /* Checks that a HIP device is present and the current one is gfx950.
  * Returns BSQ_OK or BSQ_ERR_DEVICE. */
 bsq_status bsq_device_check(void);
+/* Timing hook for benchmarks.  The next GEMM kernel that this thread
+ * launches, through any matmul entry point, is launched with
+ * hipExtLaunchKernel and records `start_event` as it begins and
+ * `stop_event` as it ends, so that hipEventElapsedTime(start, stop) is that
+ * kernel's own duration, with no marker packets around it.  Both are
+ * hipEvent_t handles owned by the caller (hipEventCreate); either may be
+ * NULL.  The request covers one kernel launch and is then cleared; both NULL
+ * clears a pending request.  Returns BSQ_OK. */
+bsq_status bsq_time_next_gemm(void* start_event, void* stop_event);
 
 /* ---------------------------------------------------------- quantizers -- */
 

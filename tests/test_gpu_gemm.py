@@ -184,6 +184,59 @@ def test_blockwise_is_deterministic():
     assert_bytes_equal(y1.view(np.uint32), y2.view(np.uint32), "two runs")
 
 
+def _hip():
+    """The process's HIP runtime (the copy torch loaded), for raw events."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    assert path is not None, "HIP runtime not loaded"
+    hip = ctypes.CDLL(path)
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (237, 4096, 4096)])
+def test_time_next_gemm_records_the_kernel(M, N, K):
+    """bsq_time_next_gemm: the next GEMM kernel records the two events (its
+    elapsed time is positive and bounded), its output is bit-identical to an
+    untimed run, and the request is used up by that one launch."""
+    import ctypes
+    torch = _torch()
+    say("time_next_gemm", M, N, K)
+    hip = _hip()
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreateWithFlags(ctypes.byref(e), 0) == 0
+    try:
+        a, b, sa, sb = _random_blockwise(M, N, K, 950)
+        y0 = host(_run_blockwise(a, b, sa, sb))
+        bsq.bsq_time_next_gemm(ev[0].value, ev[1].value)
+        y1 = host(_run_blockwise(a, b, sa, sb))
+        assert hip.hipEventSynchronize(ev[1]) == 0
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 100.0, ms.value
+        # used up: a later call leaves the events where they were
+        y2 = host(_run_blockwise(a, b, sa, sb))
+        torch.cuda.synchronize()
+        ms2 = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms2), ev[0], ev[1]) == 0
+        assert ms2.value == ms.value
+        assert_bytes_equal(y1.view(np.uint32), y0.view(np.uint32), "timed run")
+        assert_bytes_equal(y2.view(np.uint32), y0.view(np.uint32), "run after")
+        bsq.bsq_time_next_gemm(None, None)
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(e)
+
+
 def test_blockwise_group_n_1_via_scaled_matmul_f32():
     """scaled_matmul with float32 scales, block 128 on both operands (one
     B scale per row)."""
