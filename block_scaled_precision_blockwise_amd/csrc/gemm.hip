@@ -145,17 +145,20 @@ template <int MODE, int OUT_BF16, int MB, typename acc_t>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)[8][MB], uint8_t* lds_ab, int w,
                                            int lane, int batch, int m0, int n0) {
   constexpr int NB = 8;
-  static_assert(MB == 2 || MB == 4, "32 or 64 rows per wave");
+  static_assert(MB >= 2 && MB <= 4, "32, 48 or 64 rows per wave");
   const int M = p.M, N = p.N;
   const int wm = w & 3, wn = w >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   uint8_t* const stg = lds_ab + w * 32 * kStageRowB;
+  // the wave's rows in pieces of 32 (the last one 16 rows when MB is odd)
 #pragma unroll
-  for (int h = 0; h < MB / 2; ++h) {
-    if (h > 0) __syncthreads();  // the first half has been read back
+  for (int h = 0; h < (MB + 1) / 2; ++h) {
+    if (h > 0) __syncthreads();  // the previous piece has been read back
+    const int T = 2 * h + 1 < MB ? 16 : 8;  // pairs of rows in this piece
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * h + ii;
+      if (i >= MB) break;
       const int m = m0 + 16 * MB * wm + 16 * i + r16;
       float xs = 0.f;
       if (MODE == MODE_I8) xs = static_cast<const float*>(p.SA)[int64_t(batch) * p.sSA + min(m, M - 1)];
@@ -183,7 +186,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
       }
     }
     __syncthreads();
-    // rows 32 h + rr of the wave's 64: lanes 0-31 one row, 32-63 the next.
+    // rows 32 h + rr of the wave's 16 MB: lanes 0-31 one row, 32-63 the next.
     // A tile inside the matrix stores without bounds checks, so that all
     // 16 reads are issued before the first store.
     auto put = [&](int t, const float4& v) {
@@ -208,12 +211,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
     if (m0 + 64 * MB <= M && n0 + BN <= N) {
       float4 v[16];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) v[t] = get(t);
+      for (int t = 0; t < T; ++t) v[t] = get(t);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) put(t, v[t]);
+      for (int t = 0; t < T; ++t) put(t, v[t]);
     } else {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < T; ++t) {
         const int rr = 2 * t + (lane >> 5), cc = 4 * (lane & 31);
         const int m = m0 + 16 * MB * wm + 32 * h + rr;
         const int n = n0 + 128 * wn + cc;
@@ -232,7 +235,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM, int GEN = 0>
 __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   static_assert(NW == 8, "8 waves: the wave layout, scale staging and epilogue assume it");
-  static_assert(TBM == 256 || TBM == 128, "tile rows");
+  static_assert(TBM == 256 || TBM == 192 || TBM == 128, "tile rows");
   static_assert(!GEN || MODE == MODE_FP8G || MODE == MODE_MX, "general blocks: FP8G or MX");
   constexpr int NT = 64 * NW;          // threads
   constexpr int WGM = 4;                // waves along M
@@ -770,10 +773,31 @@ bsq_status zero_fill(void* p, int64_t bytes, hipStream_t st) {
   return launch_status("zero fill");
 }
 
-// Up to this many 256 x 256 tiles (and at least kSkinnyTiles), the big
-// kernel runs on 256 x 128-row tiles instead: twice the workgroups, which
-// still fit one pass over the 256 CUs, for 1.5x the operand bytes per flop.
-constexpr int64_t kHalfTiles = 134;
+// Tile height of the big kernel: 256, 192 or 128 rows by 256 columns, one
+// workgroup per CU, so the time is about (passes over the 256 CUs) x (time
+// of one tile).  A shorter tile moves more operand bytes per flop; measured
+// at n = 2048 and 4096, one pass of 192-row tiles takes 0.86-0.90 and of
+// 128-row tiles 0.74-0.79 of a pass of 256-row tiles (weights below, in
+// hundredths).  The height with the smallest passes x weight wins, the
+// taller on a tie: e.g. m = 3072, n = 4096 gives 192 tiles of 256 rows
+// (one pass, part idle) but exactly 256 of 192 rows (66.8 -> 59.5 us).
+constexpr int kCUs = 256;
+int tile_rows_for(int64_t M, int64_t N, int64_t batch) {
+  const int64_t cols = (N + BN - 1) / BN * batch;
+  const int rows[3] = {256, 192, 128};
+  const int weight[3] = {100, 88, 78};
+  int best = 256;
+  int64_t best_cost = -1;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t tiles = (M + rows[i] - 1) / rows[i] * cols;
+    const int64_t cost = (tiles + kCUs - 1) / kCUs * weight[i];
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = rows[i];
+    }
+  }
+  return best;
+}
 
 // Fewer 256 x 256 tiles than this and the split-K kernel is used instead
 // (the big-tile kernel would leave most of the 256 CUs idle).
@@ -815,14 +839,14 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
     }
   }
   constexpr int NW = 8;
-  if (tiles <= kHalfTiles) {
-    // doubling the tile count still fits one pass over the CUs: 128-row tiles
-    dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + 127) / 128), unsigned(batch));
+  const int rows = tile_rows_for(a.M, a.N, batch);
+  dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + rows - 1) / rows), unsigned(batch));
+  if (rows == 128)
     launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 128>, grid, dim3(64 * NW), st, a);
-  } else {
-    dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
+  else if (rows == 192)
+    launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 192>, grid, dim3(64 * NW), st, a);
+  else
     launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 256>, grid, dim3(64 * NW), st, a);
-  }
   return launch_status("gemm");
 }
 

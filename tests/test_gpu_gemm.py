@@ -33,7 +33,7 @@ def _torch():
 def _rows_sample(M, n=40, seed=0):
     g = np.random.default_rng(seed)
     base = {0, 1, M - 1, M // 2}
-    for t in (255, 256, 257, 511, 512):
+    for t in (127, 128, 129, 191, 192, 193, 255, 256, 257, 383, 384, 385, 511, 512, 575, 576):
         if t < M:
             base.add(t)
     extra = g.choice(M, size=min(n, M), replace=False)
@@ -107,6 +107,23 @@ def test_blockwise_full_compare(M, N, K):
     y = _run_blockwise(a, b, sa, sb)
     yr, T = OM.blockwise_fp8(a, b, sa, sb)
     assert_within_T(host(y), yr, T, "y")
+
+
+@pytest.mark.parametrize("M,N,K,out", [(2500, 4096, 256, "f32"), (4200, 2048, 384, "f32"),
+                                       (2500, 4096, 256, "bf16"), (3072, 4096, 128, "f32"),
+                                       (2000, 4096, 128, "f32"), (1100, 4096, 128, "f32")])
+def test_blockwise_tile_heights(M, N, K, out):
+    """Shapes whose pass count picks 192-row tiles (2500 and 3072 x 4096,
+    4200 x 2048; ragged M) or 128-row tiles (2000, 1100 x 4096), compared
+    with the oracle in full."""
+    torch = _torch()
+    say("blockwise tile heights", M, N, K, out)
+    a, b, sa, sb = _recipe_blockwise(M, N, K, 620 + M)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = host(_run_blockwise(a, b, sa, sb, out_dtype=od))
+    yr, T = OM.blockwise_fp8(a, b, sa, sb)
+    yh = y if out == "f32" else OF.decode_bf16(y)
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
 
 
 @pytest.mark.parametrize("M,N,K", [(349, 2048, 2048), (300, 384, 640), (513, 256, 256)])
@@ -421,6 +438,23 @@ def test_scaled_matmul_mx_small(lf, rf, out):
     assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
 
 
+@pytest.mark.parametrize("Bt,M,N,K", [(1, 2600, 4096, 128), (2, 1300, 2048, 256)])
+def test_scaled_matmul_mx_tile_heights(Bt, M, N, K):
+    """MX products whose pass count picks 192-row tiles (2600 x 4096) and
+    128-row tiles (2 x 1300 x 2048), full comparison."""
+    torch = _torch()
+    say("scaled_matmul mx tile heights", Bt, M, N, K)
+    a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 61), "e4m3")
+    b, _ = OQ.mx(synth.randn_f32((Bt, N, K), 62), "e4m3")
+    sa = synth.random_e8m0_codes((Bt, M, K // 32), 63)
+    sb = synth.random_e8m0_codes((Bt, N, K // 32), 64)
+    y = filled((Bt, M, N), torch.float32, float("nan"))
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=bsq.BSQ_E4M3,
+                          rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_E8M0)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, "e4m3", "e4m3", "e8m0")
+    assert_within_T(host(y), yr, T, "y")
+
+
 @pytest.mark.parametrize("lf,rf", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e5m2", "e5m2")])
 def test_scaled_matmul_mx_full_range_codes(lf, rf):
     """Uniformly random codes and scale exponents over -8..8."""
@@ -475,7 +509,8 @@ def test_scaled_matmul_mx_batched_full_size_sampled():
 
 # ---------------------------------------------------------------- int8 -----
 
-@pytest.mark.parametrize("B,Din,Dout", [(2048, 4096, 4096), (7, 256, 48), (5, 63, 6), (300, 384, 272)])
+@pytest.mark.parametrize("B,Din,Dout", [(2048, 4096, 4096), (7, 256, 48), (5, 63, 6), (300, 384, 272),
+                                        (2600, 256, 4096), (4300, 128, 2048)])
 def test_int8_matmul(B, Din, Dout):
     torch = _torch()
     say("int8 matmul", B, Din, Dout)
