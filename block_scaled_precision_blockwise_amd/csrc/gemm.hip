@@ -297,8 +297,11 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   }
   const uint32_t la_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_a + 8 * w * BK));
   const uint32_t lb_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds_b + 8 * w * BK));
+  // ks == nk (after the last step): every lane's offset lies past every
+  // slice's range (records <= 64 K <= 2^30), so the loads read zeros
+  // without touching memory and the loop body needs no branch
   auto gload_slice = [&](int ks, int st, int s) {
-    const int vk = voff + ks * BK;  // < 8 NW K
+    const int vk = ks < nk ? voff + ks * BK : (1 << 30);  // < 8 NW K
     if (s < SPWA) lds_dma16(ra[s], vk, la_base + uint32_t(st * TBM * BK + 8 * NW * s * BK));
     lds_dma16(rb[s], vk, lb_base + uint32_t(st * BN * BK + 8 * NW * s * BK));
   };
@@ -398,11 +401,11 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   // column blocks 0 .. SPW-1, between the MFMAs of the first half of the
   // step (all at the head of the step stalls the MFMA issue behind the
   // loads; spread over the whole step, the last ones land late).  The final
-  // step reloads its own tile into the idle stage so that the body has no
-  // branch.
+  // step issues its loads past the operands' ranges (no memory traffic) so
+  // that the body has no branch.
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks & 1;
-    const int kn = min(ks + 1, nk - 1);
+    const int kn = ks + 1;
     // the next group's scales during the last step of this group (the
     // buffer they go to was last read kSG steps ago)
     if (ks % kSG == kSG - 1 && ks + 1 < nk) sload((ks + 1) / kSG);
@@ -610,8 +613,10 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
   const i32x4 ra = rsrc32(A + int64_t(m0) * K, max(0, min(M - m0, SK_T)) * K);
   const i32x4 rb = rsrc32(B + int64_t(n0) * K, max(0, min(N - n0, SK_T)) * K);
   const uint32_t my_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(my));
+  // ks == k_end (after the wave's last step): offsets past every range
+  // (records <= 64 K <= 2^30; 2^30 + 56 K < 2^31), zeros, no memory traffic
   auto dma_step = [&](int ks, int st) {
-    const int vk = voff + ks * BK;
+    const int vk = ks < k_end ? voff + ks * BK : (1 << 30);
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
       lds_dma16(ra, vk + 8 * sl * K, my_addr + uint32_t(st * kStage + sl * 8 * BK));
@@ -669,8 +674,8 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
       load_step(0, cur);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int kn = min(ks + 1, k_end - 1);  // the last step reloads itself: no branch
-      dma_step(kn, 0);
+      dma_step(ks + 1, 0);  // after the last step: out of range, no traffic, no branch
+      const int kn = min(ks + 1, k_end - 1);
       load_scales(kn, na, nb, nqa, nqb);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
