@@ -565,27 +565,32 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
 
 // ---------------------------------------------------------------------------
 // Small and skinny products (few 256 x 256 tiles): split K inside the
-// workgroup.  SKW waves (4 or 8) share one 64 x 64 output tile; wave w runs
-// K-steps [w * per, (w + 1) * per) over the whole tile.  Each wave stages
-// its own A and B tiles of a step (16 KiB) in a private LDS region with the
-// big kernel's direct loads (8 rows x 128 bytes per instruction: whole cache
-// lines; loading MFMA fragments straight into registers reads 64-byte half
-// lines of 16 rows per instruction, and ran at a third of the rate) and
-// swizzle; nothing is shared, so the K loop has no barrier.  Once a step's
-// fragments are in registers the region takes the next step's tiles, which
-// are in flight while the step is multiplied.  One region per wave (not
-// two) keeps a 4-wave workgroup at 64 KiB of LDS, two per CU; a long K over
-// fewer tiles than that fills takes 8 waves per workgroup.  The SKW
-// partial tiles then meet in LDS (the stage area) and each output is the
-// sum of the partials in wave order - the result does not depend on timing.
-// Same MFMAs, scales and epilogue as k_gemm.
+// workgroup.  SKW waves (4; the template allows 8) share one 64 x 64 output
+// tile; wave w runs K-steps [w * per, (w + 1) * per) over the whole tile.
+// Each wave stages its own A and B tiles of a step (16 KiB) and the step's
+// scales (one word per row) in a private LDS region with the big kernel's
+// direct loads (8 rows x 128 bytes per instruction: whole cache lines;
+// loading MFMA fragments straight into registers reads 64-byte half lines
+// of 16 rows per instruction, and ran at a third of the rate) and swizzle;
+// nothing is shared, so the K loop has no barrier.  Once a step's
+// fragments and scales are in registers the region takes the next step's,
+// which are in flight while the step is multiplied; one wait per step
+// covers all of them (scales read with ordinary loads made the compiler
+// wait for every load in flight before their first use, which cost 30 %
+// at 237 x 4096 x 4096).  One region per wave keeps a workgroup at 66 KiB,
+// two per CU.  The SKW partial tiles then meet in LDS (the stage area) and
+// each output is the sum of the partials in wave order - the result does
+// not depend on timing.  Same MFMAs, scales and epilogue arithmetic as
+// k_gemm.
 constexpr int SK_T = 64;  // output tile edge
 
 template <int MODE, int OUT_BF16, int FA, int FB, int SKW>
 __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
   typedef typename std::conditional<MODE == MODE_I8, v4i, v4f>::type acc_t;
-  constexpr int kStage = 2 * SK_T * BK;  // A then B tile of one K-step
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sk[SKW * kStage];
+  constexpr bool kScales = MODE == MODE_FP8G || MODE == MODE_MX;
+  constexpr int kTiles = 2 * SK_T * BK;             // A then B tile of one K-step
+  constexpr int kRegion = kTiles + 2 * 64 * 4;      // + A and B scale words of the step
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sk[SKW * kRegion];
   static_assert(sizeof(acc_t) * SKW * SK_T * SK_T / 4 <= sizeof(lds_sk), "partials fit the stage area");
   acc_t (*red)[SK_T * SK_T / 4] = reinterpret_cast<acc_t (*)[SK_T * SK_T / 4]>(lds_sk);
 
@@ -601,8 +606,8 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
 
   const uint8_t* A = p.A + int64_t(batch) * p.sA;
   const uint8_t* B = p.B + int64_t(batch) * p.sB;
-  // this wave's LDS stages: stage st at + st * kStage, A rows then B rows
-  uint8_t* const my = lds_sk + w * kStage;
+  // this wave's LDS region: A rows, B rows, then 64 A and 64 B scale words
+  uint8_t* const my = lds_sk + w * kRegion;
   // direct loads: lane i of an 8-row slice fills LDS bytes [16 i, 16 i + 16)
   // of it, i.e. row i / 8, physical chunk i % 8, which holds the logical
   // chunk (i % 8) ^ (row & 7).  One descriptor per operand, built once,
@@ -613,45 +618,59 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
   const i32x4 ra = rsrc32(A + int64_t(m0) * K, max(0, min(M - m0, SK_T)) * K);
   const i32x4 rb = rsrc32(B + int64_t(n0) * K, max(0, min(N - n0, SK_T)) * K);
   const uint32_t my_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(my));
+  // Scales of a step come in with its tiles, one word per lane: FP8G the
+  // A scale of row m0 + lane and the tile's B scale (every lane the same
+  // word); MX the A and B words of rows m0 + lane, n0 + lane that hold the
+  // step's four 32-block exponents.  Rows past the operand read the last
+  // row (never stored).
+  const int64_t sa_row = MODE == MODE_FP8G ? int64_t(nk) * 4 : int64_t(K / 32);  // bytes per scale row
+  const uint8_t* const SAb = static_cast<const uint8_t*>(p.SA) + int64_t(batch) * p.sSA * (MODE == MODE_FP8G ? 4 : 1);
+  const uint8_t* const SBb = static_cast<const uint8_t*>(p.SB) + int64_t(batch) * p.sSB * (MODE == MODE_FP8G ? 4 : 1);
+  const int sa_voff = int((min(m0 + lane, M - 1) - m0) * sa_row);
+  const int sb_voff = MODE == MODE_MX ? int((min(n0 + lane, N - 1) - n0) * sa_row) : 0;
+  const uint8_t* const sa_base = SAb + int64_t(m0) * sa_row;
+  const uint8_t* const sb_base = MODE == MODE_MX ? SBb + int64_t(n0) * sa_row : SBb + int64_t(n0 / 128) * sa_row;
   // ks == k_end (after the wave's last step): offsets past every range
-  // (records <= 64 K <= 2^30; 2^30 + 56 K < 2^31), zeros, no memory traffic
-  auto dma_step = [&](int ks, int st) {
-    const int vk = ks < k_end ? voff + ks * BK : (1 << 30);
+  // (records <= 64 K <= 2^30; 2^30 + 56 K < 2^31) and empty scale
+  // descriptors: zeros, no memory traffic, no branch
+  auto dma_step = [&](int ks) {
+    const bool live = ks < k_end;
+    const int vk = live ? voff + ks * BK : (1 << 30);
+    const uint32_t base = my_addr;
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) {
-      lds_dma16(ra, vk + 8 * sl * K, my_addr + uint32_t(st * kStage + sl * 8 * BK));
-      lds_dma16(rb, vk + 8 * sl * K, my_addr + uint32_t(st * kStage + SK_T * BK + sl * 8 * BK));
+      lds_dma16(ra, vk + 8 * sl * K, base + uint32_t(sl * 8 * BK));
+      lds_dma16(rb, vk + 8 * sl * K, base + uint32_t(SK_T * BK + sl * 8 * BK));
+    }
+    if (kScales) {
+      const int so = 4 * ks;  // the step's word within a scale row (FP8G: its float; MX: its 4 bytes)
+      lds_dma4(rsrc32(sa_base + so, live ? 0x7FFFFFFF : 0), sa_voff, base + uint32_t(kTiles));
+      lds_dma4(rsrc32(sb_base + so, live ? 0x7FFFFFFF : 0), sb_voff, base + uint32_t(kTiles + 256));
     }
   };
   // fragment reads: row r's logical chunk c sits at physical chunk c ^ (r & 7)
   const int swz = r16 & 7;
   const int c0 = 16 * (g ^ swz), c1 = 16 * ((g + 4) ^ swz);
-  auto load_step = [&](int st, v8i (&f)[8]) {
-    const uint8_t* ta = my + st * kStage;
+  auto load_step = [&](v8i (&f)[8], float (&sa)[4], float& sb, int (&qa)[4], int (&qb)[4]) {
+    const uint8_t* ta = my;
     const uint8_t* tb = ta + SK_T * BK;
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(ta + kTiles);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int row = 16 * b + r16;
       f[b] = lds_frag(ta, row * BK + c0, row * BK + c1);
       f[4 + b] = lds_frag(tb, row * BK + c0, row * BK + c1);
     }
-  };
-  // per-step scales of this lane: A rows 16 i + r16, B rows (MX) or group
-  auto load_scales = [&](int ks, float (&sa)[4], float& sb, int (&qa)[4], int (&qb)[4]) {
     if (MODE == MODE_FP8G) {
-      const float* SA = static_cast<const float*>(p.SA) + int64_t(batch) * p.sSA;
-      const float* SB = static_cast<const float*>(p.SB) + int64_t(batch) * p.sSB;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = SA[int64_t(min(m0 + 16 * i + r16, M - 1)) * nk + ks];
-      sb = SB[int64_t(n0 / 128) * nk + ks];
+      for (int i = 0; i < 4; ++i) sa[i] = __uint_as_float(sw[16 * i + r16]);
+      sb = __uint_as_float(sw[64]);
     } else if (MODE == MODE_MX) {
-      const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + p.sSA * batch;
-      const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + p.sSB * batch;
-      const int kb = 4 * ks + g;  // this lane's 32-element block
+      // byte g of a row's word: this lane's 32-element block of the step
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        qa[i] = SA[int64_t(min(m0 + 16 * i + r16, M - 1)) * (K / 32) + kb];
-        qb[i] = SB[int64_t(min(n0 + 16 * i + r16, N - 1)) * (K / 32) + kb];
+        qa[i] = int((sw[16 * i + r16] >> (8 * g)) & 0xFFu);
+        qb[i] = int((sw[64 + 16 * i + r16] >> (8 * g)) & 0xFFu);
       }
     }
   };
@@ -664,19 +683,16 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
 
   if (k_begin < k_end) {
     v8i cur[8];
-    float sa[4], sb = 0.f, na[4], nb = 0.f;
-    int qa[4], qb[4], nqa[4], nqb[4];
-    dma_step(k_begin, 0);
-    load_scales(k_begin, sa, sb, qa, qb);
+    float sa[4] = {0.f, 0.f, 0.f, 0.f}, sb = 0.f;
+    int qa[4] = {0, 0, 0, 0}, qb[4] = {0, 0, 0, 0};
+    dma_step(k_begin);
     for (int ks = k_begin; ks < k_end; ++ks) {
-      // this step's tiles and scales have landed; once its fragments are in
-      // registers the stage takes the next step's tiles
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      load_step(0, cur);
+      // this step's tiles and scales have landed; once they are in
+      // registers the region takes the next step's
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      load_step(cur, sa, sb, qa, qb);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      dma_step(ks + 1, 0);  // after the last step: out of range, no traffic, no branch
-      const int kn = min(ks + 1, k_end - 1);
-      load_scales(kn, na, nb, nqa, nqb);
+      dma_step(ks + 1);  // past the last step: out of range, no traffic, no branch
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -700,13 +716,6 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
           }
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[i] = na[i];
-        qa[i] = nqa[i];
-        qb[i] = nqb[i];
-      }
-      sb = nb;
     }
   }
 
@@ -832,14 +841,11 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   if constexpr (MODE != MODE_BF16) {
     if (tiles < kSkinnyTiles && !GN1) {
       dim3 grid(unsigned((a.N + SK_T - 1) / SK_T), unsigned((a.M + SK_T - 1) / SK_T), unsigned(batch));
-      // 4 waves (64 KiB, two workgroups per CU); 8 waves (K split finer,
-      // one workgroup per CU) only for a long K over too few tiles to fill
-      // two per CU - measured faster there and slower elsewhere
-      const int64_t sk_tiles = int64_t(grid.x) * grid.y * grid.z;
-      if (sk_tiles >= 512 || a.K / BK < 64)
-        launch_gemm_kernel(k_gemm_sk<MODE, OUT_BF16, FA, FB, 4>, grid, dim3(256), st, a);
-      else
-        launch_gemm_kernel(k_gemm_sk<MODE, OUT_BF16, FA, FB, 8>, grid, dim3(512), st, a);
+      // 4 waves (66 KiB, two workgroups per CU).  With the scales brought
+      // in by the tile loads, 8 waves (K split finer) and a second LDS
+      // region per wave (two steps in flight) were slower on every shape
+      // measured (64 .. 1024 rows, K 512 .. 8192).
+      launch_gemm_kernel(k_gemm_sk<MODE, OUT_BF16, FA, FB, 4>, grid, dim3(256), st, a);
       return launch_status("gemm (split K)");
     }
   }
