@@ -444,6 +444,12 @@ def run_suite(args):
     scs = torch.empty(N, M // 32, dtype=torch.uint8, device=dev)
     ms = time_launches(lambda i: bsq.bsq_quant_mx(dY, codes, scs, axis=0, code_dtype=bsq.BSQ_E5M2), 20)
     hbm_row("quant_mx cols^T e5m2", f"{M}x{N} bf16", ms, M * N * 3 + M * N // 32)
+    # dY in both orientations (the backward's dX and dW operands) in one pass
+    codes_n = torch.empty(M, N, dtype=torch.uint8, device=dev)
+    scs_n = torch.empty(M, N // 32, dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dY, dyn=(codes_n, scs_n),
+                                                                 dyt=(codes, scs)), 20)
+    hbm_row("quant_mx dY rows + cols^T, one pass, e5m2", f"{M}x{N} bf16", ms, M * N * 4 + M * N // 16)
     _log(f"[suite] wrote {len(rows)} rows to {out_path}")
 
 

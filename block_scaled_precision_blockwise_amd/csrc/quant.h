@@ -11,6 +11,13 @@ bsq_status launch_fp8_tile128(int64_t rows, int64_t cols, const float* src, uint
                               float* scales, hipStream_t st);
 bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool src_bf16,
                      uint8_t* codes, bool e5m2, uint8_t* scales, hipStream_t st);
+// One pass over rows x cols (both multiples of 32): blocks of 32 along rows
+// into row_codes [rows, cols] / row_scales [rows, cols / 32], and blocks of
+// 32 down columns, transposed, into codes_t [cols, rows] / scales_t
+// [cols, rows / 32]; the same bytes as launch_mx with axis 1 and axis 0.
+bsq_status launch_mx_both(int64_t rows, int64_t cols, const void* src, bool src_bf16, bool e5m2,
+                          uint8_t* row_codes, uint8_t* row_scales, uint8_t* codes_t,
+                          uint8_t* scales_t, hipStream_t st);
 bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, float* xs,
                             hipStream_t st);
 bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* wq, float* ws,

@@ -251,12 +251,17 @@ __global__ void __launch_bounds__(256) k_mx_rows(const void* __restrict__ src,
 
 // Blocks of 32 down columns (axis = 0), output transposed.  A workgroup
 // takes a 64 x 64 tile through LDS; thread t writes 16 codes of output row
-// (input column) t / 4, two threads per 32-block.
-template <int SRC_BF16, int CODE>
+// (input column) t / 4, two threads per 32-block.  With ROWS = 1 the same
+// pass also quantizes along rows (axis = 1, blocks of 32 along a row: four
+// consecutive lanes of 8 values each) into row_codes / row_scales, exactly
+// as k_mx_rows does, so that a matrix needed in both orientations is read
+// once.
+template <int SRC_BF16, int CODE, int ROWS>
 __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
                                                    uint8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales, int64_t rows,
-                                                   int64_t cols) {
+                                                   int64_t cols, uint2* __restrict__ row_codes,
+                                                   uint8_t* __restrict__ row_scales) {
   constexpr int EMAX = CODE == 0 ? 8 : 15;
   __shared__ float tile[64][65];
   const int tx = threadIdx.x;
@@ -267,12 +272,25 @@ __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
   for (int s = 0; s < 2; ++s) {
     const int idx = tx + 256 * s;  // 0..511: row idx / 8, col group idx % 8
     const int r = idx >> 3, cg = (idx & 7) * 8;
+    const bool in = r0 + r < rows && c0 + cg < cols;
     float x[8];
-    if (r0 + r < rows && c0 + cg < cols) {
+    if (in) {
       load8<SRC_BF16>(src, (r0 + r) * cols + c0 + cg, x);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    }
+    if (ROWS) {
+      // lanes 4 q .. 4 q + 3 hold one row's 32-block (idx % 8 = lane % 8)
+      uint32_t m = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[i]));
+      const int E = mx_exponent<EMAX>(__uint_as_float(group_max_bits<4>(m)));
+      if (in) {
+        const int64_t f = ((r0 + r) * cols + c0 + cg) / 8;
+        row_codes[f] = make_uint2(mx_encode4<CODE>(&x[0], E), mx_encode4<CODE>(&x[4], E));
+        if ((tx & 3) == 0) row_scales[f >> 2] = uint8_t(E + 127);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) tile[r][cg + i] = x[i];
@@ -745,7 +763,8 @@ bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool
 #undef BSQ_MXR
   } else {
     dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64));
-#define BSQ_MXC(B, C) hipLaunchKernelGGL((k_mx_cols_t<B, C>), grid, 256, 0, st, src, codes, scales, rows, cols)
+#define BSQ_MXC(B, C) \
+  hipLaunchKernelGGL((k_mx_cols_t<B, C, 0>), grid, 256, 0, st, src, codes, scales, rows, cols, nullptr, nullptr)
     if (src_bf16) {
       if (e5m2) BSQ_MXC(1, 1); else BSQ_MXC(1, 0);
     } else {
@@ -754,6 +773,24 @@ bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool
 #undef BSQ_MXC
   }
   return launch_status("quant_mx");
+}
+
+bsq_status launch_mx_both(int64_t rows, int64_t cols, const void* src, bool src_bf16, bool e5m2,
+                          uint8_t* row_codes, uint8_t* row_scales, uint8_t* codes_t,
+                          uint8_t* scales_t, hipStream_t st) {
+  if (rows == 0 || cols == 0) return ok();
+  dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64));
+  uint2* rc = reinterpret_cast<uint2*>(row_codes);
+#define BSQ_MXB(B, C)                                                                              \
+  hipLaunchKernelGGL((k_mx_cols_t<B, C, 1>), grid, 256, 0, st, src, codes_t, scales_t, rows, cols, rc, \
+                     row_scales)
+  if (src_bf16) {
+    if (e5m2) BSQ_MXB(1, 1); else BSQ_MXB(1, 0);
+  } else {
+    if (e5m2) BSQ_MXB(0, 1); else BSQ_MXB(0, 0);
+  }
+#undef BSQ_MXB
+  return launch_status("quant_mx (both orientations)");
 }
 
 bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, float* xs,

@@ -655,6 +655,26 @@ def test_backward_two_calls_equal_one_call(fmt):
     assert_within_T(host(dW2), dW, T_dW, "dW")
 
 
+@pytest.mark.parametrize("fmt,M,N", [("e5m2", 1024, 768), ("e4m3", 384, 1280), ("e5m2", 8192, 4096)])
+def test_backward_dy_both_orientations_in_one_pass(fmt, M, N):
+    """dY wanted in both orientations is quantized in one pass over dY; its
+    bytes equal those of the two single-orientation quantizers (dY alone
+    along N, dY alone along M, transposed)."""
+    torch = _torch()
+    say("backward dY both orientations", fmt, M, N)
+    K = 128
+    code = bsq.BSQ_E5M2 if fmt == "e5m2" else bsq.BSQ_E4M3
+    dYd = to_dev(synth.randn_bf16_bits((M, N), 70 + M % 13)).view(torch.bfloat16)
+    both = _operand_tensors(M, N, K)
+    bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dYd, dyn=both["dyn"], dyt=both["dyt"], code_dtype=code)
+    one = _operand_tensors(M, N, K)
+    bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dYd, dyn=one["dyn"], code_dtype=code)
+    bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dYd, dyt=one["dyt"], code_dtype=code)
+    for name in ("dyn", "dyt"):
+        assert_bytes_equal(host(both[name][0]), host(one[name][0]), name + " codes")
+        assert_bytes_equal(host(both[name][1]), host(one[name][1]), name + " scales")
+
+
 def test_backward_prequantized_operands_from_the_oracle():
     """Operands quantized by the oracle on the host and handed over with
     their scales: only the two products run on the GPU."""
