@@ -96,9 +96,12 @@ class KernelTimer:
     (bsq_time_next_gemm) to launch its next GEMM kernel with
     hipExtLaunchKernel and these two events, which then hold that kernel's
     start and end on the stream it runs on.  No marker packet sits between
-    the kernels, so the step keeps its back-to-back schedule and the pair
-    measures the kernel alone (a separate hipEventRecord before the kernel
-    would also count the dispatch gap that its marker opens, ~5 us)."""
+    the kernels, so the step keeps its back-to-back schedule.  The pair
+    starts when the GEMM's dispatch begins, after the quantizer before it
+    has finished, so it also covers the launch of the GEMM's workgroups:
+    it reads about 5 us (7 %) above the kernel trace's duration of the
+    same launches.  (Events recorded around the call with hipEventRecord
+    added a marker packet and a dispatch gap of their own to every step.)"""
 
     def __init__(self, torch, launches):
         import ctypes

@@ -101,7 +101,7 @@ def test_blockwise_small_end_to_end():
 ])
 def test_blockwise_full_compare(M, N, K):
     """Recipe operands against the oracle; the small products run the
-    split-K kernel (4 waves; 8 waves for 130 x 1024 x 8192)."""
+    split-K kernel (4 waves)."""
     say("blockwise full (recipe operands)", M, N, K)
     a, b, sa, sb = _recipe_blockwise(M, N, K, 600 + M)
     y = _run_blockwise(a, b, sa, sb)
