@@ -522,6 +522,11 @@ def run_sweep(args):
             row[f"us_{name}"] = round(ms * 1e3, 2)
             row[f"TFLOP/s_{name}"] = round(tf, 1)
             row[f"pct_peak_{name}"] = round(100 * tf / PEAK_FP8_TFLOPS, 1)
+            # roofline of this shape: algorithmic bytes (codes, scales, output)
+            nbytes = M * K + N * K + (M + N // 128) * (K // 128) * 4 + M * N * (4 if name == "f32" else 2)
+            roof = min(PEAK_FP8_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3)
+            row[f"bound_{name}"] = "mfma" if roof >= PEAK_FP8_TFLOPS else "hbm"
+            row[f"pct_roofline_{name}"] = round(100 * tf / roof, 1)
             del y
         _log("[sweep] " + json.dumps(row))
         with open(out_path, "a") as f:
