@@ -174,6 +174,35 @@ def test_mx_backward_operand_full_size_sampled():
         assert_bytes_equal(hsn[r0:r0 + 64], rs, f"scales along N, rows {r0}")
 
 
+def test_fp8_rowblock_forward_activation_full_size_sampled():
+    """The large forward's activation (fp32 [65536, 4096], 65536 one-chunk
+    workgroups) and the MX row quantizer at 16384 x 4096: row bands at the
+    start, middle and end compared with the oracle byte for byte."""
+    torch = _torch()
+    M, K = 65536, 4096
+    say("fp8_rowblock full size", M, K)
+    x = synth.randn_f32((M, K), 410)
+    c = empty((M, K), torch.uint8)
+    s = empty((M, K // 128), torch.float32)
+    bsq.bsq_quant_fp8_rowblock(to_dev(x), c, s, 128)
+    hc, hs = host(c), host(s)
+    for r0 in (0, 31 * 1024 + 7, M - 40):
+        rc, rs = OQ.fp8_rowblock(x[r0:r0 + 40], 128)
+        assert_bytes_equal(hs[r0:r0 + 40].view(np.uint32), rs.view(np.uint32), f"scales rows {r0}")
+        assert_bytes_equal(hc[r0:r0 + 40], rc, f"codes rows {r0}")
+    del x, c, s
+    M2 = 16384
+    x = synth.randn_f32((M2, K), 411)
+    c = empty((M2, K), torch.uint8)
+    s = empty((M2, K // 32), torch.uint8)
+    bsq.bsq_quant_mx(to_dev(x), c, s, axis=1, code_dtype=bsq.BSQ_E4M3)
+    hc, hs = host(c), host(s)
+    for r0 in (0, 8191, M2 - 40):
+        rc, rs = OQ.mx_axis(x[r0:r0 + 40], 1, "e4m3")
+        assert_bytes_equal(hc[r0:r0 + 40], rc, f"mx codes rows {r0}")
+        assert_bytes_equal(hs[r0:r0 + 40], rs, f"mx scales rows {r0}")
+
+
 # ------------------------------------------------------------------ int8 ---
 
 def _examples():
