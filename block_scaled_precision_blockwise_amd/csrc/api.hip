@@ -395,16 +395,18 @@ bsq_status bwd_check_dims(int64_t M, int64_t N, int64_t K, int code_dtype) {
 bsq_status bwd_quantize(int64_t M, int64_t N, int64_t K, const void* dY, const void* W, const void* X,
                         bool e5, uint8_t* dyn_c, uint8_t* dyn_s, uint8_t* wt_c, uint8_t* wt_s,
                         uint8_t* dyt_c, uint8_t* dyt_s, uint8_t* xt_c, uint8_t* xt_s, hipStream_t st) {
-  bsq_status s = BSQ_OK;
-  if (dyn_c != nullptr && dyt_c != nullptr) {
-    // dY in both orientations from one read of dY
-    if ((s = launch_mx_both(M, N, dY, true, e5, dyn_c, dyn_s, dyt_c, dyt_s, st)) != BSQ_OK) return s;
-    dyn_c = dyt_c = nullptr;
-  }
-  if (dyn_c != nullptr && (s = launch_mx(M, N, 1, dY, true, dyn_c, e5, dyn_s, st)) != BSQ_OK) return s;
-  if (wt_c != nullptr && (s = launch_mx(N, K, 0, W, true, wt_c, e5, wt_s, st)) != BSQ_OK) return s;
-  if (dyt_c != nullptr && (s = launch_mx(M, N, 0, dY, true, dyt_c, e5, dyt_s, st)) != BSQ_OK) return s;
-  if (xt_c != nullptr && (s = launch_mx(M, K, 0, X, true, xt_c, e5, xt_s, st)) != BSQ_OK) return s;
+  // the transposed operands in one launch; dY in both orientations from
+  // one read of dY when both are wanted
+  MxT jobs[3];
+  int n = 0;
+  const bool dy_both = dyn_c != nullptr && dyt_c != nullptr;
+  if (dyt_c != nullptr) jobs[n++] = MxT{dY, M, N, dyt_c, dyt_s, dy_both ? dyn_c : nullptr, dyn_s};
+  if (wt_c != nullptr) jobs[n++] = MxT{W, N, K, wt_c, wt_s, nullptr, nullptr};
+  if (xt_c != nullptr) jobs[n++] = MxT{X, M, K, xt_c, xt_s, nullptr, nullptr};
+  bsq_status s = launch_mx_cols(jobs, n, true, e5, st);
+  if (s != BSQ_OK) return s;
+  if (dyn_c != nullptr && !dy_both && (s = launch_mx(M, N, 1, dY, true, dyn_c, e5, dyn_s, st)) != BSQ_OK)
+    return s;
   return ok();
 }
 

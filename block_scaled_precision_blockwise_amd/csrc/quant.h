@@ -11,13 +11,21 @@ bsq_status launch_fp8_tile128(int64_t rows, int64_t cols, const float* src, uint
                               float* scales, hipStream_t st);
 bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool src_bf16,
                      uint8_t* codes, bool e5m2, uint8_t* scales, hipStream_t st);
-// One pass over rows x cols (both multiples of 32): blocks of 32 along rows
-// into row_codes [rows, cols] / row_scales [rows, cols / 32], and blocks of
-// 32 down columns, transposed, into codes_t [cols, rows] / scales_t
-// [cols, rows / 32]; the same bytes as launch_mx with axis 1 and axis 0.
-bsq_status launch_mx_both(int64_t rows, int64_t cols, const void* src, bool src_bf16, bool e5m2,
-                          uint8_t* row_codes, uint8_t* row_scales, uint8_t* codes_t,
-                          uint8_t* scales_t, hipStream_t st);
+// Blocks of 32 down the columns of up to three matrices in one launch, each
+// rows x cols (both multiples of 32) from src: codes_t [cols, rows] and
+// scales_t [cols, rows / 32], the bytes of launch_mx with axis 0.  A job
+// with row_codes set also writes blocks of 32 along its rows into
+// row_codes [rows, cols] / row_scales [rows, cols / 32] (the bytes of
+// launch_mx with axis 1) from the same read of src.
+struct MxT {
+  const void* src;
+  int64_t rows, cols;
+  uint8_t* codes_t;
+  uint8_t* scales_t;
+  uint8_t* row_codes;
+  uint8_t* row_scales;
+};
+bsq_status launch_mx_cols(const MxT* jobs, int n, bool src_bf16, bool e5m2, hipStream_t st);
 bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, float* xs,
                             hipStream_t st);
 bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* wq, float* ws,

@@ -253,22 +253,44 @@ __global__ void __launch_bounds__(256) k_mx_rows(const void* __restrict__ src,
 
 // Blocks of 32 down columns (axis = 0), output transposed.  A workgroup
 // takes a 64 x 64 tile through LDS; thread t writes 16 codes of output row
-// (input column) t / 4, two threads per 32-block.  With ROWS = 1 the same
-// pass also quantizes along rows (axis = 1, blocks of 32 along a row: four
-// consecutive lanes of 8 values each) into row_codes / row_scales, exactly
+// (input column) t / 4, two threads per 32-block.  A launch covers up to
+// kMxJobs matrices (the backward's three transposed operands in one grid):
+// workgroup b belongs to the job whose range of tiles holds it.  A job with
+// row_codes set also quantizes along rows (axis = 1, blocks of 32 along a
+// row: four consecutive lanes of 8 values each) in the same pass, exactly
 // as k_mx_rows does, so that a matrix needed in both orientations is read
 // once.
-template <int SRC_BF16, int CODE, int ROWS>
-__global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
-                                                   uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales, int64_t rows,
-                                                   int64_t cols, uint2* __restrict__ row_codes,
-                                                   uint8_t* __restrict__ row_scales) {
+constexpr int kMxJobs = 3;
+struct MxJob {
+  const void* src;
+  uint8_t* codes;      // [cols, rows]
+  uint8_t* scales;     // [cols, rows / 32]
+  uint2* row_codes;    // [rows, cols] or null
+  uint8_t* row_scales; // [rows, cols / 32]
+  int64_t rows, cols;
+  int tiles_x;         // 64-column tiles
+  int first;           // first workgroup of the job
+};
+struct MxJobs {
+  MxJob j[kMxJobs];
+  int n;
+};
+
+template <int SRC_BF16, int CODE>
+__global__ void __launch_bounds__(256) k_mx_cols_t(MxJobs jobs) {
   constexpr int EMAX = CODE == 0 ? 8 : 15;
   __shared__ float tile[64][65];
+  int ji = 0;
+#pragma unroll
+  for (int q = 1; q < kMxJobs; ++q)
+    if (q < jobs.n && int(blockIdx.x) >= jobs.j[q].first) ji = q;
+  const MxJob& J = jobs.j[ji];
+  const int t = int(blockIdx.x) - J.first;
+  const int64_t rows = J.rows, cols = J.cols;
   const int tx = threadIdx.x;
-  const int64_t r0 = int64_t(blockIdx.y) * 64;
-  const int64_t c0 = int64_t(blockIdx.x) * 64;
+  const int64_t r0 = int64_t(t / J.tiles_x) * 64;
+  const int64_t c0 = int64_t(t % J.tiles_x) * 64;
+  const bool both = J.row_codes != nullptr;
   // load: 64 rows x 64 cols, 8 values per thread-step, 2 steps
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -277,12 +299,12 @@ __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
     const bool in = r0 + r < rows && c0 + cg < cols;
     float x[8];
     if (in) {
-      load8<SRC_BF16>(src, (r0 + r) * cols + c0 + cg, x);
+      load8<SRC_BF16>(J.src, (r0 + r) * cols + c0 + cg, x);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = 0.f;
     }
-    if (ROWS) {
+    if (both) {
       // lanes 4 q .. 4 q + 3 hold one row's 32-block (idx % 8 = lane % 8)
       uint32_t m = 0u;
 #pragma unroll
@@ -290,8 +312,8 @@ __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
       const int E = mx_exponent<EMAX>(__uint_as_float(group_max_bits<4>(m)));
       if (in) {
         const int64_t f = ((r0 + r) * cols + c0 + cg) / 8;
-        row_codes[f] = make_uint2(mx_encode4<CODE>(&x[0], E), mx_encode4<CODE>(&x[4], E));
-        if ((tx & 3) == 0) row_scales[f >> 2] = uint8_t(E + 127);
+        J.row_codes[f] = make_uint2(mx_encode4<CODE>(&x[0], E), mx_encode4<CODE>(&x[4], E));
+        if ((tx & 3) == 0) J.row_scales[f >> 2] = uint8_t(E + 127);
       }
     }
 #pragma unroll
@@ -313,8 +335,8 @@ __global__ void __launch_bounds__(256) k_mx_cols_t(const void* __restrict__ src,
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[q] = mx_encode4<CODE>(&x[4 * q], E);
-    *reinterpret_cast<uint4*>(codes + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
-    if ((seg & 1) == 0) scales[orow * (rows / 32) + (ocol >> 5)] = uint8_t(E + 127);
+    *reinterpret_cast<uint4*>(J.codes + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
+    if ((seg & 1) == 0) J.scales[orow * (rows / 32) + (ocol >> 5)] = uint8_t(E + 127);
   }
 }
 
@@ -764,35 +786,41 @@ bsq_status launch_mx(int64_t rows, int64_t cols, int axis, const void* src, bool
     }
 #undef BSQ_MXR
   } else {
-    dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64));
-#define BSQ_MXC(B, C) \
-  hipLaunchKernelGGL((k_mx_cols_t<B, C, 0>), grid, 256, 0, st, src, codes, scales, rows, cols, nullptr, nullptr)
-    if (src_bf16) {
-      if (e5m2) BSQ_MXC(1, 1); else BSQ_MXC(1, 0);
-    } else {
-      if (e5m2) BSQ_MXC(0, 1); else BSQ_MXC(0, 0);
-    }
-#undef BSQ_MXC
+    const MxT job{src, rows, cols, codes, scales, nullptr, nullptr};
+    return launch_mx_cols(&job, 1, src_bf16, e5m2, st);
   }
   return launch_status("quant_mx");
 }
 
-bsq_status launch_mx_both(int64_t rows, int64_t cols, const void* src, bool src_bf16, bool e5m2,
-                          uint8_t* row_codes, uint8_t* row_scales, uint8_t* codes_t,
-                          uint8_t* scales_t, hipStream_t st) {
-  if (rows == 0 || cols == 0) return ok();
-  dim3 grid(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64));
-  uint2* rc = reinterpret_cast<uint2*>(row_codes);
-#define BSQ_MXB(B, C)                                                                              \
-  hipLaunchKernelGGL((k_mx_cols_t<B, C, 1>), grid, 256, 0, st, src, codes_t, scales_t, rows, cols, rc, \
-                     row_scales)
-  if (src_bf16) {
-    if (e5m2) BSQ_MXB(1, 1); else BSQ_MXB(1, 0);
-  } else {
-    if (e5m2) BSQ_MXB(0, 1); else BSQ_MXB(0, 0);
+bsq_status launch_mx_cols(const MxT* jobs, int n, bool src_bf16, bool e5m2, hipStream_t st) {
+  MxJobs J{};
+  int blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (jobs[i].rows == 0 || jobs[i].cols == 0) continue;
+    if (J.n == kMxJobs) return fail(BSQ_ERR_UNSUPPORTED, "quant_mx: too many matrices in one launch");
+    MxJob& j = J.j[J.n++];
+    j.src = jobs[i].src;
+    j.codes = jobs[i].codes_t;
+    j.scales = jobs[i].scales_t;
+    j.row_codes = reinterpret_cast<uint2*>(jobs[i].row_codes);
+    j.row_scales = jobs[i].row_scales;
+    j.rows = jobs[i].rows;
+    j.cols = jobs[i].cols;
+    j.tiles_x = int((jobs[i].cols + 63) / 64);
+    j.first = blocks;
+    const int64_t tiles = int64_t(j.tiles_x) * ((jobs[i].rows + 63) / 64);
+    if (blocks + tiles > int64_t(INT32_MAX)) return fail(BSQ_ERR_UNSUPPORTED, "quant_mx: too many tiles");
+    blocks += int(tiles);
   }
-#undef BSQ_MXB
-  return launch_status("quant_mx (both orientations)");
+  if (J.n == 0) return ok();
+#define BSQ_MXC(B, C) hipLaunchKernelGGL((k_mx_cols_t<B, C>), dim3(unsigned(blocks)), 256, 0, st, J)
+  if (src_bf16) {
+    if (e5m2) BSQ_MXC(1, 1); else BSQ_MXC(1, 0);
+  } else {
+    if (e5m2) BSQ_MXC(0, 1); else BSQ_MXC(0, 0);
+  }
+#undef BSQ_MXC
+  return launch_status("quant_mx (columns, transposed)");
 }
 
 bsq_status launch_int8_rows(int64_t B, int64_t D, const float* x, int8_t* xq, float* xs,
