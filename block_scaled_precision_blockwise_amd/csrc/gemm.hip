@@ -1,5 +1,5 @@
 // Block-scaled GEMM for gfx950: out[m, n] = sum_k A[m, k] B[n, k] with the
-// scales of the three modes this library runs.
+// scales of the four modes this library runs.
 //
 //   FP8G  E4M3 operands, float32 scales per 128-wide K-block: one
 //         v_mfma_f32_16x16x128_f8f6f4 per K-block (exactly one 128-group),
@@ -11,12 +11,17 @@
 //         matrix core and accumulates directly (scaled_matmul with mxfp8).
 //   I8    int8 operands, v_mfma_i32_16x16x64_i8 into int32 accumulators,
 //         float32 epilogue float(a) * (s_x * s_w) (int8 per-channel).
+//   BF16  bfloat16 operands (nvfp4 after its exact dequantization),
+//         v_mfma_f32_16x16x32_bf16, no scales.
 //
 // Both operands are K-contiguous ("TN").  A workgroup of 8 waves owns a
-// 256 x 256 output tile and walks K in steps of 128; each step's A and B
-// tiles (32 KiB each) are double-buffered in LDS with a 16-byte-chunk XOR
-// swizzle so the fragment reads are free of bank conflicts.  Wave (wm, wn)
-// owns rows 64*wm..+64 and columns 128*wn..+128: 4 x 8 blocks of 16 x 16.
+// 256 x 256 output tile (192 or 128 rows when that fills the CUs in fewer
+// passes) and walks K in steps of 128 bytes; each step's A and B tiles are
+// double-buffered in LDS with a 16-byte-chunk XOR swizzle so the fragment
+// reads are free of bank conflicts.  Wave (wm, wn) owns a quarter of the
+// rows and columns 128*wn..+128: 4 (3, 2) x 8 blocks of 16 x 16.  Products
+// with few tiles run k_gemm_sk instead (64 x 64 tiles, K split over the
+// workgroup's waves).
 //
 // Fragment layout (measured on gfx950): for the 16x16x128 f8 MFMA a lane
 // l supplies 32 bytes of row l % 16: K [16g, 16g+16) in bytes 0..15 and K
@@ -228,7 +233,8 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
 }
 
 // NW = 8 waves per workgroup: waves 4 (M) x 2 (N), each 64 x 128 (4 x 8
-// blocks), accumulators in VGPRs - the FP8G rescale needs them on the VALU.
+// blocks; 48 or 32 rows for TBM = 192 or 128), accumulators in VGPRs - the
+// FP8G rescale needs them on the VALU.
 // (Measured alternatives that were not faster: 4 waves of 128 x 128 with
 // AGPR accumulators; two wave groups alternating between MFMA and memory
 // phases with a barrier per phase; an L2 prefetch two steps ahead.)
