@@ -302,19 +302,29 @@ def run_suite(args):
     os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
     rows = []
 
-    def time_launches(fn, n_iter, rotate=1):
+    last = {}
+
+    def time_launches(fn, n_iter, rotate=1, reps=5):
+        """Median over `reps` batches of the per-launch time of a batch of
+        n_iter back-to-back launches (the minimum is kept for the row)."""
         for i in range(3):
             fn(i % rotate)
         torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
-        _queue_ahead(torch)
-        s.record()
-        for i in range(n_iter):
-            fn(i % rotate)
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / n_iter  # ms
+        per = []
+        for r in range(reps):
+            _queue_ahead(torch)
+            s.record()
+            for i in range(n_iter):
+                fn((r * n_iter + i) % rotate)
+            e.record()
+            torch.cuda.synchronize()
+            per.append(s.elapsed_time(e) / n_iter)
+        per.sort()
+        last["min_ms"] = per[0]
+        last["launches"] = reps * n_iter
+        return per[len(per) // 2]  # ms
 
     def emit(row):
         rows.append(row)
@@ -324,12 +334,14 @@ def run_suite(args):
 
     def hbm_row(name, workload, ms, nbytes):
         gbs = nbytes / (ms * 1e-3) / 1e9
-        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2), "bytes": int(nbytes),
+        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2),
+              "us_min": round(last["min_ms"] * 1e3, 2), "launches": last["launches"], "bytes": int(nbytes),
               "GB/s": round(gbs, 1), "pct_hbm": round(100 * gbs / PEAK_HBM_GBS, 1)})
 
     def mfma_row(name, workload, ms, flops, peak):
         tf = flops / (ms * 1e-3) / 1e12
-        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2), "flops": flops,
+        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2),
+              "us_min": round(last["min_ms"] * 1e3, 2), "launches": last["launches"], "flops": flops,
               "TFLOP/s": round(tf, 1), "pct_peak": round(100 * tf / peak, 1)})
 
     open(out_path, "w").close()
@@ -355,6 +367,17 @@ def run_suite(args):
         ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(a, b, sa, sb, y), n_it)
         mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} g128 f32 out", ms, 2 * M * N * K, PEAK_FP8_TFLOPS)
         del a, b, sa, sb, y
+    # ---- the same GEMM cold: 16 operand sets (512 MiB of codes) rotated, so
+    # the 256 MB cache cannot hold the operands between launches
+    M = N = K = 4096
+    ops = [(torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev),
+            torch.randint(0, 126, (N, K), dtype=torch.uint8, device=dev),
+            torch.rand(M, K // 128, device=dev), torch.rand(N // 128, K // 128, device=dev)) for _ in range(16)]
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(*ops[i], y), 16, 16)
+    mfma_row("gemm_fp8_blockwise (cold operands)", f"{M}x{N}x{K} g128 f32 out, 16 rotating operand sets", ms,
+             2 * M * N * K, PEAK_FP8_TFLOPS)
+    del ops, y
     # ---- general groups (the same kernel, general scale indexing)
     M = N = K = 4096
     a = torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev)
@@ -421,7 +444,17 @@ def run_suite(args):
                                                        scale_dtype=bsq.BSQ_E8M0), 10)
     mfma_row("gemm_mx_batched", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/64 f32 out", ms, 2 * Bt * M * N * K,
              PEAK_FP8_TFLOPS)
-    del lhs32, lq, ls, rq, ym
+    del lhs32, ls
+    # cold: 4 operand sets (512 MiB of codes) rotated
+    mops = [(lq.view(Bt, M, K), rq.view(Bt, N, K))] + [
+        (torch.randint(0, 126, (Bt, M, K), dtype=torch.uint8, device=dev),
+         torch.randint(0, 126, (Bt, N, K), dtype=torch.uint8, device=dev)) for _ in range(3)]
+    ms = time_launches(lambda i: bsq.bsq_scaled_matmul(mops[i][0], mops[i][1], sa, sb, ym,
+                                                       lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3,
+                                                       scale_dtype=bsq.BSQ_E8M0), 8, 4)
+    mfma_row("gemm_mx_batched (cold operands)", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/32 f32 out, 4 rotating operand sets",
+             ms, 2 * Bt * M * N * K, PEAK_FP8_TFLOPS)
+    del mops, lq, rq, ym
     # ---- MXFP8 backward
     M, N, K = 8192, 4096, 4096
     dY = torch.randn(M, N, device=dev).to(torch.bfloat16)
