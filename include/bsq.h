@@ -92,8 +92,8 @@ bsq_status bsq_time_next_gemm(void* start_event, void* stop_event);
  *   src    float32 [rows, cols]
  *   codes  uint8   [rows, cols]          (E4M3 bytes, out)
  *   scales float32 [rows, cols / group]  (out)
- * Rules: cols % group == 0, group % 32 == 0 and group <= 1024; rows may be
- * 0. */
+ * Rules: cols % group == 0 (else BSQ_ERR_SHAPE); group is 32, 64, 128 or
+ * 256 (else BSQ_ERR_UNSUPPORTED); rows may be 0. */
 bsq_status bsq_quant_fp8_rowblock(int64_t rows, int64_t cols, int64_t group,
                                   const float* src, uint8_t* codes, float* scales,
                                   void* stream);

@@ -53,6 +53,7 @@ def test_fp8_rowblock_validation(L):
     _expect(f(-1, 128, 128, A16, A16, A16, None), SHAPE, L)
     _expect(f(4, 100, 128, A16, A16, A16, None), SHAPE, L)      # cols % group
     _expect(f(4, 144, 48, A16, A16, A16, None), UNSUP, L)      # group 48
+    _expect(f(4, 1024, 512, A16, A16, A16, None), UNSUP, L)    # group 512 (32, 64, 128, 256 only)
     _expect(f(4, 128, 128, None, A16, A16, None), NULL, L)
     _expect(f(4, 128, 128, A4, A16, A16, None), ALIGN, L)
     _expect(f(0, 128, 128, None, None, None, None), OK, L)     # empty is a no-op
