@@ -355,7 +355,15 @@ def run_suite(args):
         st = torch.empty(R // 128, C // 128, dtype=torch.float32, device=dev)
         ms = time_launches(lambda i: bsq.bsq_quant_fp8_tile(xs[i], codes, st, 128, 128), 40, 8)
         hbm_row("quant_fp8_tile 128x128", f"{R}x{C} f32", ms, R * C * 5 + st.numel() * 4)
-        del xs
+        del codes, sc, st, xs
+    # the large forward's activation (1 GiB of fp32: larger than the cache by itself)
+    for (R, C) in [(65536, 4096)]:
+        xl = torch.randn(R, C, device=dev)
+        codes = torch.empty(R, C, dtype=torch.uint8, device=dev)
+        sc = torch.empty(R, C // 128, dtype=torch.float32, device=dev)
+        ms = time_launches(lambda i: bsq.bsq_quant_fp8_rowblock(xl, codes, sc, 128), 10)
+        hbm_row("quant_fp8_rowblock 1x128", f"{R}x{C} f32 (large forward activation)", ms, R * C * 5 + R * C // 128 * 4)
+        del xl, codes, sc
     # ---- FP8 GEMM sweep
     for (M, N, K) in [(256, 512, 512)] + list(synth.FP8_SWEEP) + [(65536, 4096, 4096)]:
         a = torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev)
@@ -420,6 +428,12 @@ def run_suite(args):
     hbm_row("int8_quant_cols+T", f"{Din}x{Dout} f32 (w_q and w_qT)", ms, Din * Dout * 6 + Dout * 4)
     ms = time_launches(lambda i: bsq.bsq_int8_matmul(xq, wqT, xsc, wsc, yi), 20)
     mfma_row("gemm_int8", f"{B}x{Dout}x{Din} i32 acc, f32 epilogue", ms, 2 * B * Din * Dout, PEAK_INT8_TOPS)
+    # the whole problem: both quantizers and the GEMM
+    wk = torch.empty(max(bsq.bsq_int8_workspace_bytes(Din, Dout), 16), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_int8_per_channel_matmul(x, w, wq, wsc, xq, xsc, yi, wk), 20)
+    mfma_row("int8_per_channel (quantize x and w, GEMM)", f"{B}x{Dout}x{Din}", ms, 2 * B * Din * Dout,
+             PEAK_INT8_TOPS)
+    del wk
     del x, w, xq, wq, wqT, yi
     # ---- MXFP8 batched scaled_matmul
     Bt, M, N, K = 8, 2048, 2048, 4096
