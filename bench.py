@@ -17,7 +17,7 @@ sample on this host.
     python bench.py --suite [--out FILE]
 times every kernel of the path at its own workload (quantizers, FP8 GEMM
 sweep, INT8 per-channel, MXFP8 batched, MXFP8 backward) and writes one JSON
-object per kernel to FILE (default gpurun_out/suite.jsonl).
+object per kernel to FILE (default bench_out/suite.jsonl).
 
 One GPU only: --gpus N with N > 1 exits with a message.
 """
@@ -45,7 +45,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PAGE_T_PROD_TFLOPS_4096 = 2 * 4096 ** 3 / 1.06e-3 / 1e12
 GEMM_SRC = os.path.join(ROOT, "block_scaled_precision_blockwise_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fp8_4096_traffic.json")
-DEFAULT_SUITE_OUT = os.path.join(ROOT, "gpurun_out", "suite.jsonl")
+DEFAULT_SUITE_OUT = os.path.join(ROOT, "bench_out", "suite.jsonl")
 
 
 def _log(*a):
@@ -622,7 +622,7 @@ def main():
         run_suite(args)
     elif args.sweep:
         if args.out == DEFAULT_SUITE_OUT:
-            args.out = os.path.join(ROOT, "gpurun_out", "sweep.jsonl")
+            args.out = os.path.join(ROOT, "bench_out", "sweep.jsonl")
         run_sweep(args)
     else:
         run_main(args)

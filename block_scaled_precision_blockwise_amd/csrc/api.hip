@@ -211,7 +211,7 @@ bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t gro
   BSQ_CHECK(known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown out_dtype");
   BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
             "out_dtype must be F32 or BF16");
-  BSQ_CHECK(group_k % 128 == 0, BSQ_ERR_UNSUPPORTED, "this build runs group_k multiples of 128");
+  BSQ_CHECK(group_k % 128 == 0, BSQ_ERR_UNSUPPORTED, "the library runs group_k multiples of 128");
   BSQ_CHECK(N % 16 == 0, BSQ_ERR_UNSUPPORTED, "N must be a multiple of 16");
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
@@ -259,7 +259,7 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
   BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
             "out_dtype must be F32 or BF16");
   BSQ_CHECK(K % 128 == 0 && N % 16 == 0, BSQ_ERR_UNSUPPORTED,
-            "this build needs K % 128 == 0 and N % 16 == 0");
+            "the library needs K % 128 == 0 and N % 16 == 0");
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
   GemmLaunch L{};
@@ -595,7 +595,7 @@ bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, c
   BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
             "out_dtype must be F32 or BF16");
   BSQ_CHECK(K % 128 == 0 && N % 16 == 0, BSQ_ERR_UNSUPPORTED,
-            "this build needs K % 128 == 0 and N % 16 == 0");
+            "the library needs K % 128 == 0 and N % 16 == 0");
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction / 2,
             BSQ_ERR_UNSUPPORTED, "extent too large");
   const size_t need = bsq_nvfp4_workspace_bytes(B, M, N, K);

@@ -105,7 +105,7 @@ bsq_status bsq_quant_fp8_rowblock(int64_t rows, int64_t cols, int64_t group,
  *   src    float32 [rows, cols]
  *   codes  uint8   [rows, cols]                        (E4M3, out)
  *   scales float32 [rows / group_r, cols / group_c]    (out)
- * Rules: rows % group_r == 0, cols % group_c == 0; this build runs
+ * Rules: rows % group_r == 0, cols % group_c == 0; the library runs
  * group_r == group_c == 128. */
 bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64_t group_c,
                               const float* src, uint8_t* codes, float* scales, void* stream);
@@ -154,7 +154,7 @@ bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8
  *   a_scales float32 [M, K / group_k]
  *   b_scales float32 [N / group_n, K / group_k]
  *   out      [M, N], out_dtype BSQ_F32 or BSQ_BF16 (nearest even)
- * Rules: N % group_n == 0, K % group_k == 0; M >= 0 arbitrary.  This build
+ * Rules: N % group_n == 0, K % group_k == 0; M >= 0 arbitrary.  The library
  * runs any group_n (N % 16 == 0) and group_k a multiple of 128; other
  * group_k -> UNSUPPORTED.  group_k == 128 with group_n 1 or 128 is the
  * tuned kernel; other groups run the same kernel with general scale
@@ -170,7 +170,7 @@ bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t gro
  *   lhs [B, M, K], rhs [B, N, K] codes (lhs_dtype / rhs_dtype E4M3 or E5M2)
  *   lhs_scales [B, M, K_a], rhs_scales [B, N, K_b] of scale_dtype
  *   out [B, M, N] of out_dtype (BSQ_F32, the page's default, or BSQ_BF16)
- * Rules: K % K_a == 0 and K % K_b == 0 (else SHAPE).  This build runs
+ * Rules: K % K_a == 0 and K % K_b == 0 (else SHAPE).  The library runs
  * (K % 128 == 0, N % 16 == 0): scale_dtype E8M0 with blocks K / K_a and
  * K / K_b multiples of 32 (they may differ; unless both are 32, K_a and
  * K_b must be multiples of 4); scale_dtype F32 with E4M3 operands and
@@ -187,7 +187,7 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
  *   x_q  [B, D_in] int8;  w_qT [D_out, D_in] int8 (w_q transposed, as
  *   written by bsq_int8_quant_cols);  x_s [B], w_s [D_out] float32
  *   y [B, D_out] float32 (out); acc [B, D_out] int32 (out) or NULL.
- * Rules: D_in % 128 == 0 in this build (else UNSUPPORTED). */
+ * Rules: D_in % 128 == 0 in the library (else UNSUPPORTED). */
 bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t* x_q,
                            const int8_t* w_qT, const float* x_s, const float* w_s, float* y,
                            int32_t* acc, void* stream);
@@ -275,7 +275,7 @@ bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dt
  *       receives both operands dequantized to bfloat16 (exact: an e2m1
  *       value times an e4m3 scale has at most 6 significant bits), which
  *       a bf16 matrix-core product then multiplies in float32.
- * Rules: K % 16 == 0 (else SHAPE); this build needs K % 128 == 0 and
+ * Rules: K % 16 == 0 (else SHAPE); the library needs K % 128 == 0 and
  * N % 16 == 0 (else UNSUPPORTED); a smaller workspace -> SHAPE. */
 size_t bsq_nvfp4_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K);
 bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, const uint8_t* lhs,
