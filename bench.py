@@ -8,10 +8,12 @@ group_n = group_k = 128: quantize the float32 activations (1 x 128 blocks,
 E4M3 + float32 scales), quantize the float32 weights (128 x 128 tiles), then
 the block-scaled GEMM with its fused float32 epilogue.  Inputs are resident
 in HBM before timing; four input sets are rotated so that the 256 MB
-last-level cache cannot serve the quantizers' reads.  `value` is the GEMM's
-algorithmic 2 m n k FLOPs per step time (TFLOP/s).  The JSON line also
-carries the GEMM kernel's own roofline (HIP events around each of its
-launches, on the launch stream) and the CPU oracle timed on a bounded
+last-level cache cannot serve the quantizers' reads.  After settling steps
+(the clocks of an idle GPU ramp up over the first ~150 steps) and the W
+warm-up steps, K plain steps give `value`: the GEMM's algorithmic 2 m n k
+FLOPs per step time (TFLOP/s).  A second pass of K steps, whose GEMM
+launches carry HIP events on the launch stream, gives the GEMM kernel's own
+roofline.  The JSON line also carries the CPU oracle timed on a bounded
 sample on this host.
 
     python bench.py --suite [--out FILE]
