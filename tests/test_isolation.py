@@ -3,7 +3,8 @@
 The product (the package and its HIP sources) never imports, includes or
 links anything under oracle/; the oracle never imports the package; the
 seeded input generators in synth/ import neither.  Checked on the sources'
-import statements and #include lines, so it runs without a GPU.
+import statements and #include lines, so it runs without a GPU.  Without
+libbsq.so the binding raises instead of computing anything.
 """
 import ast
 import os
@@ -78,3 +79,29 @@ def test_build_links_no_oracle_code():
     for node in ast.walk(tree):
         if isinstance(node, ast.Constant) and isinstance(node.value, str) and node.value.endswith((".hip", ".c", ".o")):
             assert "oracle" not in node.value, node.value
+
+
+def test_binding_fails_loudly_without_the_library():
+    """With libbsq.so absent every call raises; nothing computes elsewhere."""
+    import subprocess
+    import sys
+    code = (
+        "import block_scaled_precision_blockwise_amd as b, torch\n"
+        "b._LIB_PATH = '/nonexistent/libbsq.so'\n"
+        "b._lib = None\n"
+        "try:\n"
+        "    b.bsq_version()\n"
+        "    raise SystemExit('bsq_version returned without the library')\n"
+        "except RuntimeError as e:\n"
+        "    assert 'libbsq.so' in str(e), e\n"
+        "x = torch.randn(4, 128)\n"
+        "q = torch.empty(4, 128, dtype=torch.uint8)\n"
+        "s = torch.empty(4, 1)\n"
+        "try:\n"
+        "    b.bsq_quant_fp8_rowblock(x, q, s, 128)\n"
+        "    raise SystemExit('a quantizer returned without the library')\n"
+        "except (RuntimeError, ValueError):\n"
+        "    pass\n"
+        "print('ok')\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
