@@ -126,6 +126,25 @@ def test_blockwise_tile_heights(M, N, K, out):
     assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
 
 
+@pytest.mark.parametrize("M,N,K,out", [(1792, 2304, 512, "f32"), (2048, 2048, 512, "f32"),
+                                       (1793, 2304, 512, "f32"), (1792, 2432, 512, "f32"),
+                                       (1500, 2176, 384, "bf16"), (1700, 2432, 384, "bf16")])
+def test_blockwise_kernel_switch(M, N, K, out):
+    """Both sides of the switch between the split-K kernel (fewer than 64
+    output tiles of 256 x 256) and the tiled kernel: 7 x 9 = 63 tiles, 8 x 8
+    = 64, one more row (8 x 9 = 72), a half tile of N (7 x 10 = 70), and the
+    same with ragged M and bfloat16 output (6 x 9 = 54 split-K, 7 x 10
+    tiled); compared with the oracle in full."""
+    torch = _torch()
+    say("blockwise kernel switch", M, N, K, out)
+    a, b, sa, sb = _recipe_blockwise(M, N, K, 640 + M + N)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = host(_run_blockwise(a, b, sa, sb, out_dtype=od))
+    yr, T = OM.blockwise_fp8(a, b, sa, sb)
+    yh = y if out == "f32" else OF.decode_bf16(y)
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
+
+
 @pytest.mark.parametrize("M,N,K", [(349, 2048, 2048), (300, 384, 640), (513, 256, 256)])
 def test_blockwise_full_range_codes(M, N, K):
     say("blockwise full (random codes)", M, N, K)
