@@ -457,6 +457,30 @@ def test_scaled_matmul_mx_small(lf, rf, out):
     assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
 
 
+@pytest.mark.parametrize("Bt,M,N,K,out", [(3, 768, 1792, 256, "f32"), (2, 1024, 2048, 256, "f32"),
+                                          (3, 769, 1792, 256, "f32"), (1, 1000, 2000, 256, "bf16"),
+                                          (2, 1000, 2000, 256, "bf16")])
+def test_scaled_matmul_mx_kernel_switch(Bt, M, N, K, out):
+    """Both sides of the switch between the split-K kernel and the tiled
+    kernel, where the batch counts in the tiles: 3 x 3 x 7 = 63 tiles of
+    256 x 256, 2 x 4 x 8 = 64, one more row (3 x 4 x 7 = 84), and N = 2000
+    (a 16-column tail in the last 64- and 256-wide tile) at 32 and 64
+    tiles; compared with the oracle in full."""
+    torch = _torch()
+    say("scaled_matmul mx kernel switch", Bt, M, N, K, out)
+    a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 61 + M), "e4m3")
+    b, _ = OQ.mx(synth.randn_f32((Bt, N, K), 62 + N), "e4m3")
+    sa = synth.random_e8m0_codes((Bt, M, K // 32), 63)
+    sb = synth.random_e8m0_codes((Bt, N, K // 32), 64)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    y = filled((Bt, M, N), od, float("nan"))
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=bsq.BSQ_E4M3,
+                          rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_E8M0)
+    yr, T = OM.scaled_matmul(a, b, sa, sb, "e4m3", "e4m3", "e8m0")
+    yh = host(y) if out == "f32" else OF.decode_bf16(host(y))
+    assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
+
+
 @pytest.mark.parametrize("Bt,M,N,K", [(1, 2600, 4096, 128), (2, 1300, 2048, 256)])
 def test_scaled_matmul_mx_tile_heights(Bt, M, N, K):
     """MX products whose pass count picks 192-row tiles (2600 x 4096) and
