@@ -11,14 +11,18 @@ fp8_rowblock / fp8_tile
     tile's max without abs(); the activation path and the workload
     description both use the absolute maximum, which is the reading taken
     here for both (a signed max would let negative outliers clip).
-    Parity pinned by invariants (the pages print no quantized values).
+    The pages print no quantized values.  Pinned by invariants, by each
+    float32 division (scale and quotient) recomputed as an exact rational
+    rounded to nearest even, and by the recipe re-derived with torch CPU
+    ops and torch's own float8 cast.
 
 int8_rows / int8_cols
     TensorTonic "Int8 Matmul with Per-Channel Scales": s = max|v| / 127 per
     row of x and per column of w, s = 1 for an all-zero row or column,
     q = clip(round(v / s), -127, 127) with round = nearest, ties to even
     (the problem's hint names jnp.round, which rounds half to even).
-    Pinned by the three printed examples.
+    Pinned by the three printed examples, by exact-rational rounding of
+    the scale and quotient divisions, and by a torch CPU re-derivation.
 
 mx
     MX blocks of 32 along the contraction axis with an e8m0 scale
@@ -28,8 +32,7 @@ mx
     and restrict the scale to a power of two by rounding it up: E is the
     smallest integer with absmax <= fmax * 2^E, clamped to [-127, 127],
     scale byte = E + 127, codes = fp8(clamp(x * 2^-E, +-fmax)).  No element
-    ever clips.  ``rule="ocp"`` gives the OCP-style alternative
-    E = floor(log2 absmax) - emax_elem with saturation, for comparison only.
+    ever clips.
     Parity unpinned by the pages for the scale rule itself; pinned by
     invariants and by the power-of-two special case that coincides with
     fp8_rowblock.
@@ -120,32 +123,27 @@ def _exponent_fields(a: np.ndarray):
     return e, mant
 
 
-def mx_scale_exponent(amax: np.ndarray, fmt: str, rule: str = "ceil") -> np.ndarray:
-    """Block scale exponent E (int64) for float32 block maxima."""
+def mx_scale_exponent(amax: np.ndarray, fmt: str) -> np.ndarray:
+    """Block scale exponent E (int64) for float32 block maxima: the smallest
+    E with max(amax, 1e-10) <= fmax * 2^E, clamped to [-127, 127]."""
     amax = np.maximum(_f32(amax), F32_1E_10)
     e, mant = _exponent_fields(amax)
-    if rule == "ceil":
-        # smallest E with amax <= fmax * 2^E, computed exactly: fmax is
-        # 1.75 * 2^emax_elem for both formats, so with amax = (1+f) 2^e the
-        # answer is e - emax_elem, plus one when 1+f exceeds 1.75.
-        top = F.fmax(fmt)
-        emax_elem = int(np.floor(np.log2(top)))
-        top_mant = top / 2.0 ** emax_elem  # 1.75
-        top_mant_bits = int(round((top_mant - 1.0) * (1 << 23)))
-        E = e - emax_elem + (mant > top_mant_bits).astype(np.int64)
-        # exact cross-check of the defining inequality (float64 holds all)
-        a64 = amax.astype(np.float64)
-        assert np.all(a64 <= top * np.exp2(E.astype(np.float64)))
-        assert np.all(a64 > top * np.exp2(E.astype(np.float64) - 1))
-    elif rule == "ocp":
-        emax_elem = {F.E4M3: 8, F.E5M2: 15}[fmt]
-        E = e - emax_elem
-    else:
-        raise ValueError(rule)
+    # computed exactly: fmax is 1.75 * 2^emax_elem for both formats, so with
+    # amax = (1+f) 2^e the answer is e - emax_elem, plus one when 1+f
+    # exceeds 1.75.
+    top = F.fmax(fmt)
+    emax_elem = int(np.floor(np.log2(top)))
+    top_mant = top / 2.0 ** emax_elem  # 1.75
+    top_mant_bits = int(round((top_mant - 1.0) * (1 << 23)))
+    E = e - emax_elem + (mant > top_mant_bits).astype(np.int64)
+    # exact cross-check of the defining inequality (float64 holds all)
+    a64 = amax.astype(np.float64)
+    assert np.all(a64 <= top * np.exp2(E.astype(np.float64)))
+    assert np.all(a64 > top * np.exp2(E.astype(np.float64) - 1))
     return np.clip(E, -127, 127)
 
 
-def mx(x: np.ndarray, fmt: str = F.E4M3, block: int = 32, rule: str = "ceil"):
+def mx(x: np.ndarray, fmt: str = F.E4M3, block: int = 32):
     """MX quantization of x[..., C] with ``block``-element blocks along the
     last axis.
 
@@ -159,7 +157,7 @@ def mx(x: np.ndarray, fmt: str = F.E4M3, block: int = 32, rule: str = "ceil"):
     lead = x.shape[:-1]
     xb = x.reshape(*lead, C // block, block)
     amax = np.max(np.abs(xb), axis=-1) if xb.size else np.zeros((*lead, C // block), np.float32)
-    E = mx_scale_exponent(amax, fmt, rule)
+    E = mx_scale_exponent(amax, fmt)
     # x * 2^-E is exact in float32 for every value that stays normal; those
     # that underflow encode to a signed zero either way.
     v = np.ldexp(xb, (-E)[..., None].astype(np.int32)).astype(np.float32)

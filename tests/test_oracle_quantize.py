@@ -4,7 +4,9 @@ int8: the three worked examples of the int8 per-channel problem (codes
 exact, scales and outputs to the printed 6 decimals).  fp8 and MX: the pages
 print no quantized values, so these are pinned by invariants that a wrong
 max (signed instead of absolute), a wrong block index, a dropped floor or a
-reciprocal instead of a division would break.
+reciprocal instead of a division would break; every float32 division is also
+recomputed as an exact rational rounded by the IEEE definition, and the
+recipes are re-derived with torch CPU ops.
 """
 import json
 import os
@@ -317,3 +319,224 @@ def test_mx_axis_layout():
     c2, s2 = Q.mx_axis(x, 1, F.E5M2)
     c3, s3 = Q.mx_axis(y, 1, F.E5M2)
     assert np.argwhere(s2 != s3).tolist() == [[40, 0]]
+
+
+# ------------------------------------------- float32 rounding, independently ---
+# The scales and quotients of the fp8 and int8 quantizers are float32
+# divisions (block_scaled_mm, Input Generation: absmax / 448 and x / scale;
+# int8 per-channel: max|v| / 127 and v / s).  These pins recompute each
+# division as an exact rational and round it to float32 by the IEEE-754
+# definition (nearest, ties to the even significand), with no float
+# division anywhere, so a scale or quotient that is one ulp off (e.g. from a
+# reciprocal multiply) fails them.
+
+from fractions import Fraction
+
+
+def _f32_nearest(q: Fraction) -> np.float32:
+    """float32 nearest to the rational q (ties to even), normal or
+    subnormal; |q| below 2^128."""
+    if q == 0:
+        return np.float32(0.0)
+    neg = q < 0
+    a = -q if neg else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    # now 2^e <= a < 2^(e+1); quantum of the significand's last place
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    v = np.float32(float(lo * quantum))  # lo * quantum is exactly a float32
+    assert Fraction(float(v)) == lo * quantum
+    return np.float32(-v) if neg else v
+
+
+def test_f32_nearest_helper_against_known_values():
+    # the helper itself: exact values, a tie to even, subnormals
+    assert _f32_nearest(Fraction(1, 3)) == np.float32(1.0) / np.float32(3.0)
+    one = Fraction(1)
+    ulp = Fraction(1, 1 << 23)
+    assert _f32_nearest(one + ulp / 2) == np.float32(1.0)              # tie -> even
+    assert _f32_nearest(one + 3 * ulp / 2) == np.float32(1.0 + 2 * 2.0 ** -23)  # tie -> even
+    assert _f32_nearest(Fraction(1, 1 << 149)) == np.float32(2.0 ** -149)
+    assert _f32_nearest(Fraction(1, 1 << 150)) == np.float32(0.0)      # tie -> even (0)
+    assert _f32_nearest(Fraction(-7, 2)) == np.float32(-3.5)
+
+
+def _recip_multiply_differs(amax: np.float32, d: int) -> bool:
+    r = np.float32(np.float32(1.0) / np.float32(d))
+    return np.float32(amax * r) != _f32_nearest(Fraction(float(amax)) / d)
+
+
+def _amax_where_reciprocal_fails(d: int, count: int, seed: int):
+    """float32 values a with f32(a * RN(1/d)) != RN(a / d)."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        a = np.float32(g.uniform(0.01, 100.0))
+        if _recip_multiply_differs(a, d):
+            out.append(a)
+    return np.array(out, np.float32)
+
+
+def test_fp8_scale_is_the_correctly_rounded_quotient():
+    """s = float32(amax / 448) exactly (then floored at float32(1e-10)),
+    for random block maxima across binades and for maxima where amax times
+    RN(1/448) rounds to a different float32."""
+    g = np.random.default_rng(31)
+    hard = _amax_where_reciprocal_fails(448, 64, 32)
+    amaxes = np.concatenate([
+        hard,
+        (g.standard_normal(256) * np.exp2(g.integers(-40, 40, 256))).astype(np.float32),
+        np.array([448.0, 1.0, 3.0, 7.7316003, 1e-9, 4.48e-8, 4.4799997e-8, 3e38], np.float32),
+    ])
+    n = len(amaxes)
+    x = synth.randn_f32((n, 128), 33) * np.float32(1e-3)
+    x = np.clip(x, -np.abs(amaxes)[:, None], np.abs(amaxes)[:, None])
+    x[:, 5] = amaxes                    # the block maximum (sign kept)
+    _, s = Q.fp8_rowblock(x, 128)
+    floor = np.float32(1e-10)
+    for i in range(n):
+        want = _f32_nearest(Fraction(float(abs(amaxes[i]))) / 448)
+        want = max(want, floor)
+        assert s[i, 0] == want, (i, float(amaxes[i]), float(s[i, 0]), float(want))
+    # the tile quantizer takes the same division (one tile per maximum)
+    xt = np.zeros((128, 128 * 16), np.float32)
+    for j in range(16):
+        xt[7 * j, 128 * j + j] = -hard[j]
+    _, st = Q.fp8_tile(xt, 128, 128)
+    for j in range(16):
+        assert st[0, j] == _f32_nearest(Fraction(float(hard[j])) / 448)
+    # and these maxima do separate a reciprocal multiply from the division
+    assert all(_recip_multiply_differs(a, 448) for a in hard[:16])
+
+
+def test_int8_scale_is_the_correctly_rounded_quotient():
+    hard = _amax_where_reciprocal_fails(127, 48, 34)
+    g = np.random.default_rng(35)
+    amaxes = np.concatenate([hard, (np.abs(g.standard_normal(64)) * np.exp2(g.integers(-30, 30, 64)))
+                             .astype(np.float32)])
+    x = synth.randn_f32((len(amaxes), 24), 36) * np.float32(1e-4)
+    x = np.clip(x, -amaxes[:, None], amaxes[:, None])
+    x[:, 3] = -amaxes
+    _, s = Q.int8_rows(x)
+    for i, a in enumerate(amaxes):
+        assert s[i] == _f32_nearest(Fraction(float(a)) / 127), (i, float(a))
+    _, sw = Q.int8_cols(np.ascontiguousarray(x.T))
+    assert np.array_equal(sw, s)
+
+
+def _midpoint_values(fmt: str):
+    """Positive fp8 midpoints between consecutive finite values."""
+    t = np.sort(np.unique(np.abs(F.decode_table(fmt)[np.isfinite(F.decode_table(fmt))])))
+    return (t[:-1] + t[1:]) / 2.0
+
+
+def test_fp8_codes_use_the_correctly_rounded_quotient():
+    """Elements placed so that x / s lies on or next to an e4m3 rounding
+    midpoint: each code equals the encoding of the exactly rounded quotient
+    RN(x / s).  A quotient one float32 ulp off moves such codes."""
+    mids = _midpoint_values(F.E4M3)
+    g = np.random.default_rng(37)
+    rows = []
+    for r in range(24):
+        amax = np.float32(g.uniform(0.5, 2.0) * 2.0 ** int(g.integers(-20, 20)))
+        s = np.float32(amax / np.float32(448))
+        blk = np.zeros(128, np.float32)
+        blk[0] = amax
+        pick = g.choice(mids, 127)
+        for i, m in enumerate(pick):
+            # x near m * s: the float32 nearest, and its neighbours
+            base = _f32_nearest(Fraction(float(m)) * Fraction(float(s)))
+            blk[1 + i] = [base, np.nextafter(base, np.float32(np.inf)),
+                          np.nextafter(base, np.float32(0))][i % 3] * (1 if i % 2 else -1)
+        rows.append(blk)
+    x = np.stack(rows)
+    codes, s = Q.fp8_rowblock(x, 128)
+    top = Fraction(448)
+    for r in range(x.shape[0]):
+        sr = Fraction(float(s[r, 0]))
+        q = [_f32_nearest(Fraction(float(v)) / sr) for v in x[r]]
+        q = np.array([float(max(-top, min(top, Fraction(float(v))))) for v in q], np.float32)
+        want = F.encode(q, F.E4M3)
+        assert np.array_equal(codes[r], want), r
+
+
+def test_int8_codes_use_the_correctly_rounded_quotient():
+    """Elements with x / s on or next to a half-integer: codes follow
+    rint(RN(x / s)) with the quotient rounded exactly."""
+    g = np.random.default_rng(38)
+    rows = []
+    for r in range(24):
+        amax = np.float32(g.uniform(0.5, 2.0) * 2.0 ** int(g.integers(-20, 20)))
+        s = np.float32(amax / np.float32(127))
+        v = np.zeros(96, np.float32)
+        v[0] = amax
+        for i in range(1, 96):
+            h = Fraction(int(g.integers(0, 127))) + Fraction(1, 2)
+            base = _f32_nearest(h * Fraction(float(s)))
+            v[i] = [base, np.nextafter(base, np.float32(np.inf)), np.nextafter(base, np.float32(0))][i % 3]
+        rows.append(v)
+    x = np.stack(rows)
+    xq, xs = Q.int8_rows(x)
+    for r in range(x.shape[0]):
+        sr = Fraction(float(xs[r]))
+        for i in range(x.shape[1]):
+            qf = Fraction(float(_f32_nearest(Fraction(float(x[r, i])) / sr)))
+            lo = qf.numerator // qf.denominator
+            rem = qf - lo
+            n = lo + (1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2) else 0)
+            assert int(xq[r, i]) == max(-127, min(127, n)), (r, i)
+
+
+def test_fp8_quantizers_equal_a_torch_cpu_rederivation():
+    """The block_scaled_mm recipe written again with torch CPU tensor ops
+    (abs-max, float32 division, clamp, torch's own float8_e4m3fn cast):
+    codes and scales equal the oracle's byte for byte."""
+    torch = pytest.importorskip("torch")
+    x = synth.randn_f32((64, 512), 39)
+    x[3, 128:256] = 0.0
+    x[5, :128] *= np.float32(1e-13)
+    x[9, 300] = -40.0
+    t = torch.from_numpy(x)
+    lim = torch.tensor(448.0, dtype=torch.float32)
+    floor = torch.tensor(1e-10, dtype=torch.float32)
+    # 1 x 128 along rows
+    tb = t.view(64, 4, 128)
+    st = torch.maximum(tb.abs().amax(dim=2) / lim, floor)
+    ct = torch.clamp(tb / st[:, :, None], -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes, s = Q.fp8_rowblock(x, 128)
+    assert np.array_equal(s.view(np.uint32), st.numpy().view(np.uint32))
+    assert np.array_equal(codes, ct.reshape(64, 512).numpy())
+    # 128 x 128 tiles (absolute maximum, reading R1)
+    xt = synth.randn_f32((256, 384), 40)
+    xt[200, 10] = -25.0
+    tt = torch.from_numpy(xt).view(2, 128, 3, 128)
+    stt = torch.maximum(tt.abs().amax(dim=(1, 3)) / lim, floor)
+    ctt = torch.clamp(tt / stt[:, None, :, None], -448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes_t, s_t = Q.fp8_tile(xt, 128, 128)
+    assert np.array_equal(s_t.view(np.uint32), stt.numpy().view(np.uint32))
+    assert np.array_equal(codes_t, ctt.reshape(256, 384).numpy())
+
+
+def test_int8_quantizers_equal_a_torch_cpu_rederivation():
+    torch = pytest.importorskip("torch")
+    x, w = synth.int8_workload(40, 96, 24, 41, 42, zero_rows=(3,), zero_cols=(5,))
+    tx = torch.from_numpy(x)
+    amax = tx.abs().amax(dim=1, keepdim=True)
+    s = torch.where(amax == 0, torch.ones_like(amax), amax / 127.0)
+    q = torch.clamp(torch.round(tx / s), -127, 127).to(torch.int8)   # torch.round: half to even
+    xq, xs = Q.int8_rows(x)
+    assert np.array_equal(xq, q.numpy())
+    assert np.array_equal(xs.view(np.uint32), s.squeeze(1).numpy().view(np.uint32))
+    tw = torch.from_numpy(w)
+    amw = tw.abs().amax(dim=0, keepdim=True)
+    sw = torch.where(amw == 0, torch.ones_like(amw), amw / 127.0)
+    qw = torch.clamp(torch.round(tw / sw), -127, 127).to(torch.int8)
+    wq, ws = Q.int8_cols(w)
+    assert np.array_equal(wq, qw.numpy())
+    assert np.array_equal(ws.view(np.uint32), sw.squeeze(0).numpy().view(np.uint32))
