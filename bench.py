@@ -274,40 +274,75 @@ def run_main(args):
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline():
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(runs: int = 3):
     """The oracle as written, on one whole step of the same workload: both
     quantizers, then the oracle GEMM (its float64 product and its
-    error-bound product).  About 10 s on 8 cores; reported as TFLOP/s on
-    the GEMM's 2 m n k."""
+    error-bound product), with the BLAS thread pool set to the cores this
+    process may run on (its affinity mask, capped by OMP_NUM_THREADS).  The median of `runs` runs (about 4 s each on 16
+    cores) is reported as TFLOP/s on the GEMM's 2 m n k."""
     import numpy as np
     import synth
     from oracle import matmul as OM
     from oracle import quantize as OQ
 
+    affinity = len(os.sched_getaffinity(0))
+    # the host's share for this process: its affinity mask, capped by the
+    # thread count the environment grants (a shared GPU host may show more
+    # CPUs than one job may use)
+    want = affinity
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        want = min(want, int(os.environ.get("OMP_NUM_THREADS", affinity)))
+    except ValueError:
+        pass
+    limit = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limit = threadpool_limits(limits=want, user_api="blas")
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                      or [want])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = want
     M = N = K = 4096
     rows = 4096
     a32, b32 = synth.fp8_blockwise_raw(M, N, K, 204, 205)
-    _log(f"[bench] cpu baseline: oracle on {rows} of {M} rows ...")
-    t0 = time.perf_counter()
-    a, sa = OQ.fp8_rowblock(a32[:rows])
-    b, sb = OQ.fp8_tile(b32)
-    y, T = OM.blockwise_fp8(a, b, sa, sb)
-    dt = time.perf_counter() - t0
+    _log(f"[bench] cpu baseline: oracle on {rows} of {M} rows, {runs} runs, {threads} BLAS threads ...")
+    times = []
+    try:
+        for r in range(runs):
+            t0 = time.perf_counter()
+            a, sa = OQ.fp8_rowblock(a32[:rows])
+            b, sb = OQ.fp8_tile(b32)
+            y, T = OM.blockwise_fp8(a, b, sa, sb)
+            times.append(time.perf_counter() - t0)
+            _log(f"[bench] cpu baseline run {r}: {times[-1]:.2f} s")
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+    dt = sorted(times)[len(times) // 2]
     flops = 2.0 * rows * N * K
-    _log(f"[bench] cpu baseline: {dt:.2f} s -> {flops / dt / 1e12:.5f} TFLOP/s")
+    _log(f"[bench] cpu baseline: median {dt:.2f} s -> {flops / dt / 1e12:.5f} TFLOP/s")
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"one full step ({rows}x4096x4096): oracle 1x128 and 128x128 quantizers + float64 "
-                  f"blockwise GEMM with its error-bound GEMM; {dt:.2f} s",
+                  f"blockwise GEMM with its error-bound GEMM; median of {runs} runs",
         "seconds": round(dt, 3),
+        "runs_s": [round(t, 3) for t in times],
+        "affinity_cpus": affinity,
+        "cpu_model": _cpu_model(),
     }
 
 

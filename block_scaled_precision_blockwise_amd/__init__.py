@@ -207,7 +207,6 @@ def bsq_quant_fp8_tile(src, codes, scales, group_r: int = 128, group_c: int = 12
     """src f32 [rows, cols] -> codes u8 [rows, cols], scales f32
     [rows/group_r, cols/group_c]."""
     torch = _torch()
-    _dev(src, codes, scales)
     rows, cols = src.shape
     _expect(src, torch.float32, (rows, cols), "src")
     _bytes1(codes, "codes")
@@ -215,6 +214,12 @@ def bsq_quant_fp8_tile(src, codes, scales, group_r: int = 128, group_c: int = 12
         raise ValueError("codes shape")
     if scales.dtype != torch.float32:
         raise TypeError("scales must be float32")
+    if group_r > 0 and group_c > 0:
+        # an undersized scale tensor would be written past its end
+        sshape = (rows // group_r, cols // group_c)
+        if tuple(scales.shape) != sshape:
+            raise ValueError(f"scales must have shape {sshape}, got {tuple(scales.shape)}")
+    _dev(src, codes, scales)
     _raise(lib().bsq_quant_fp8_tile(rows, cols, group_r, group_c, _ptr(src), _ptr(codes), _ptr(scales),
                                     _stream(stream)), "bsq_quant_fp8_tile")
 
@@ -301,6 +306,16 @@ def bsq_scaled_matmul(lhs, rhs, lhs_scales, rhs_scales, out, lhs_dtype=None, rhs
     [B, M, K_a], rhs_scales [B, N, K_b] (E8M0 bytes or f32); out [B, M, N]
     f32 or bf16."""
     torch = _torch()
+    # dtypes first (a wrong scale width would make the kernel read past the
+    # scale arrays), then the device checks
+    _bytes1(lhs, "lhs")
+    _bytes1(rhs, "rhs")
+    if scale_dtype == BSQ_E8M0:
+        _bytes1(lhs_scales, "lhs_scales (E8M0)")
+        _bytes1(rhs_scales, "rhs_scales (E8M0)")
+    elif scale_dtype == BSQ_F32:
+        if lhs_scales.dtype != torch.float32 or rhs_scales.dtype != torch.float32:
+            raise TypeError("F32 scales must be float32 tensors")
     _dev(lhs, rhs, lhs_scales, rhs_scales, out)
     B, M, K = lhs.shape
     N = rhs.shape[1]

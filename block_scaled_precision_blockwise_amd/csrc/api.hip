@@ -313,12 +313,18 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
   return launch_gemm(L, as_stream(stream));
 }
 
+// Longest int8 contraction whose int32 sums cannot wrap: |a| <= 127^2 D_in
+// stays at or below 2^31 - 1 (the problem's sums are int32).
+constexpr int64_t kMaxInt8Contraction = (int64_t(0x7FFFFFFF)) / (127 * 127);  // 133144
+
 bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t* x_q,
                            const int8_t* w_qT, const float* x_s, const float* w_s, float* y,
                            int32_t* acc, void* stream) {
   BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
-  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30) && D_in <= kMaxContraction,
-            BSQ_ERR_UNSUPPORTED, "extent too large");
+  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30), BSQ_ERR_UNSUPPORTED,
+            "extent too large");
+  BSQ_CHECK(D_in <= kMaxInt8Contraction, BSQ_ERR_UNSUPPORTED,
+            "D_in > 133144: int32 sums of int8 products could wrap");
   if (B == 0 || D_out == 0) return ok();
   BSQ_CHECK_PTR(y);
   BSQ_CHECK(x_s != nullptr && w_s != nullptr, BSQ_ERR_NULL, "scales are NULL");
@@ -353,6 +359,8 @@ bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, c
   BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
   BSQ_CHECK(workspace_bytes >= bsq_int8_workspace_bytes(D_in, D_out), BSQ_ERR_SHAPE,
             "workspace too small");
+  BSQ_CHECK(D_in <= kMaxInt8Contraction, BSQ_ERR_UNSUPPORTED,
+            "D_in > 133144: int32 sums of int8 products could wrap");
   if (D_in > 0 && D_out > 0) BSQ_CHECK_PTR(workspace);
   bsq_status s = bsq_int8_quant_rows(B, D_in, x, x_q, x_s, stream);
   if (s != BSQ_OK) return s;

@@ -321,53 +321,55 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   // of a scale row instead of one word of kSG of them), for the group of
   // steps that follows the current one.
   // Lane i of wave w fills slot 64 w + i (waves 0-3 the A rows, 4-7 the B
-  // rows).  Lanes with nothing to move read row 0 of their operand's scales
+  // rows).  Lanes with nothing to move read their wave's first scale row
   // into a slot nobody reads.
   constexpr bool kScales = MODE == MODE_FP8G || MODE == MODE_MX;
   static_assert(!kScales || NW == 8, "scale staging assumes 512 threads");
-  const uint8_t* sbase = nullptr;  // this wave's scale array at K-step 0
-  int soff_v = 0;                  // this lane's byte offset in it
-  int64_t s_records = 0;
+  // Each wave's scale base starts at the first scale row its lanes read
+  // (64-bit arithmetic, once per workgroup); a lane's offset from it stays
+  // below 256 rows of at most 2^19 bytes, so it fits 32 bits whatever M
+  // and N are.
+  const uint8_t* sbase = nullptr;  // this wave's scale rows at K-step 0
+  int soff_v = 0;                  // this lane's byte offset from sbase
+  int64_t s_records = 0;           // bytes from sbase to the end of the scale array
   int s_per = 1;                   // GEN: this wave's K-steps (FP8G) / 32-blocks (MX) per scale
-  if (kScales && GEN) {
-    // general blocks: a scale row holds sc scales; B rows of the FP8G
-    // kernel are output columns, gn of them per scale row
-    const bool a_side = w < 4;
-    const int r = tid - 256;
-    const int esz = MODE == MODE_FP8G ? 4 : 1;
-    const int cols = a_side ? p.sc_a : p.sc_b;
-    s_per = a_side ? p.sg_a : p.sg_b;
-    const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + int64_t(batch) * p.sSA * esz;
-    const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + int64_t(batch) * p.sSB * esz;
-    const int rows_b = MODE == MODE_FP8G ? N / p.gn : N;
-    sbase = a_side ? SA : SB;
-    s_records = (a_side ? int64_t(M) : int64_t(rows_b)) * cols * esz;
-    // B rows: MX per column; FP8G per column (GN1) or, when group_n is a
-    // multiple of 128, per 128-column half of the tile (slots 256, 257)
-    const int row_b = MODE == MODE_MX ? min(n0 + r, N - 1)
-                      : GN1 ? min(n0 + r, N - 1) / p.gn
-                            : ((r >= 0 && r < 2 && n0 + 128 * r < N) ? (n0 + 128 * r) / p.gn : 0);
-    const int row = a_side ? min(m0 + tid, M - 1) : row_b;
-    soff_v = row * cols * esz;
-  } else if (kScales) {
+  if (kScales) {
     // waves 0-3 (uniform w < 4) own the A slots, waves 4-7 the B slots
     const bool a_side = w < 4;
     const int r = tid - 256;
-    if (MODE == MODE_FP8G) {
-      const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + int64_t(batch) * p.sSA * 4;
-      const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + int64_t(batch) * p.sSB * 4;
-      const int rows_b = GN1 ? N : N / 128;
-      sbase = a_side ? SA : SB;
-      s_records = (a_side ? int64_t(M) : int64_t(rows_b)) * nk * 4;
-      const int rb = GN1 ? min(n0 + r, N - 1) : ((r >= 0 && r < 2 && n0 + 128 * r < N) ? n0 / 128 + r : 0);
-      soff_v = (a_side ? min(m0 + tid, M - 1) : rb) * nk * 4;
+    const int esz = MODE == MODE_FP8G ? 4 : 1;
+    const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + int64_t(batch) * p.sSA * esz;
+    const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + int64_t(batch) * p.sSB * esz;
+    // bytes per scale row, scale rows of each operand, and this lane's row
+    // next to the wave's first row (rows past the operand read its last row)
+    int row_bytes, rows_op, row, row0;
+    if (GEN) {
+      // general blocks: a scale row holds sc scales; B rows of the FP8G
+      // kernel are output columns, gn of them per scale row
+      row_bytes = (a_side ? p.sc_a : p.sc_b) * esz;
+      s_per = a_side ? p.sg_a : p.sg_b;
+      rows_op = a_side ? M : (MODE == MODE_FP8G ? N / p.gn : N);
     } else {
-      const uint8_t* SA = static_cast<const uint8_t*>(p.SA) + p.sSA * batch;
-      const uint8_t* SB = static_cast<const uint8_t*>(p.SB) + p.sSB * batch;
-      sbase = a_side ? SA : SB;
-      s_records = (a_side ? int64_t(M) : int64_t(N)) * nk * 4;
-      soff_v = (a_side ? min(m0 + tid, M - 1) : min(n0 + r, N - 1)) * nk * 4;
+      row_bytes = nk * 4;  // FP8G: one float per K-step; MX: K / 32 bytes
+      rows_op = a_side ? M : (MODE == MODE_FP8G && !GN1 ? N / 128 : N);
     }
+    if (a_side) {
+      row0 = m0;
+      row = min(m0 + tid, M - 1);
+    } else if (MODE == MODE_MX || GN1) {
+      // B scale row per output column
+      row0 = MODE == MODE_FP8G && GEN ? n0 / p.gn : n0;
+      row = MODE == MODE_FP8G && GEN ? min(n0 + r, N - 1) / p.gn : min(n0 + r, N - 1);
+    } else {
+      // FP8G with one B scale per 128 (GEN: group_n, a multiple of 128)
+      // columns: slots 256 and 257 hold the tile's two column halves
+      const int gdiv = GEN ? p.gn : 128;
+      row0 = n0 / gdiv;
+      row = (r >= 0 && r < 2 && n0 + 128 * r < N) ? (n0 + 128 * r) / gdiv : row0;
+    }
+    sbase = (a_side ? SA : SB) + int64_t(row0) * row_bytes;
+    s_records = int64_t(rows_op - row0) * row_bytes;
+    soff_v = (row - row0) * row_bytes;
   }
   const uint32_t ls_base =
       __builtin_amdgcn_readfirstlane(lds_addr_of(reinterpret_cast<const uint8_t*>(&lds_s[0][64 * w * kSG])));

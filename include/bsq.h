@@ -187,7 +187,11 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
  *   x_q  [B, D_in] int8;  w_qT [D_out, D_in] int8 (w_q transposed, as
  *   written by bsq_int8_quant_cols);  x_s [B], w_s [D_out] float32
  *   y [B, D_out] float32 (out); acc [B, D_out] int32 (out) or NULL.
- * Rules: D_in % 128 == 0 in the library (else UNSUPPORTED). */
+ * Rules: D_in <= 133144, so that no int32 sum can wrap (127^2 D_in <=
+ * 2^31 - 1); larger -> UNSUPPORTED.  Shapes with D_in % 128 == 0,
+ * D_out % 16 == 0 and 16-byte aligned x_q, w_qT, w_s run on the int8 matrix
+ * core; any other shape runs a plain per-output kernel with the same
+ * arithmetic (slower, same results). */
 bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t* x_q,
                            const int8_t* w_qT, const float* x_s, const float* w_s, float* y,
                            int32_t* acc, void* stream);
@@ -196,7 +200,8 @@ bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t*
  * columns, multiply in int8 with int32 sums, apply the float32 epilogue.
  * Writes the five results the problem returns (w_q, w_scales, x_q,
  * x_scales, y).  `workspace` holds the transposed weight codes: at least
- * bsq_int8_workspace_bytes(D_in, D_out) bytes, 16-byte aligned. */
+ * bsq_int8_workspace_bytes(D_in, D_out) bytes, 16-byte aligned.  Rules as
+ * bsq_int8_matmul (D_in <= 133144), checked before anything is enqueued. */
 size_t bsq_int8_workspace_bytes(int64_t D_in, int64_t D_out);
 bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, const float* x,
                                        const float* w, int8_t* w_q, float* w_s, int8_t* x_q,

@@ -205,3 +205,47 @@ def test_nvfp4_validation(L):
     _expect(f(1, 16, 32, 256, A16, A16, None, A16, A16, F32, A16, need, None), NULL, L)
     _expect(f(0, 16, 32, 256, None, None, None, None, None, F32, None, 0, None), OK, L)
     _expect(f(1, 16, 32, 256, A16, A16, A16, A16, A16, BF, A16, need, None), DEVICE, L)
+
+
+def test_int8_contraction_limit(L):
+    """The int32 sums of int8 products (int8 per-channel, output formula)
+    cannot wrap while 127^2 D_in <= 2^31 - 1, i.e. D_in <= 133144; longer
+    contractions are refused before anything is enqueued, by the matmul and
+    by the composite."""
+    assert 127 * 127 * 133144 <= 2 ** 31 - 1 < 127 * 127 * 133145
+    _expect(L.bsq_int8_matmul(2, 133144, 16, A16, A16, A16, A16, A16, None, None), DEVICE, L)
+    _expect(L.bsq_int8_matmul(2, 133145, 16, A16, A16, A16, A16, A16, None, None), UNSUP, L)
+    need = L.bsq_int8_workspace_bytes(133145, 16)
+    _expect(L.bsq_int8_per_channel_matmul(2, 133145, 16, A16, A16, A16, A16, A16, A16, A16, A16,
+                                          need, None), UNSUP, L)
+    need = L.bsq_int8_workspace_bytes(133144, 16)
+    _expect(L.bsq_int8_per_channel_matmul(2, 133144, 16, A16, A16, A16, A16, A16, A16, A16, A16,
+                                          need, None), DEVICE, L)
+
+
+def test_binding_checks_scale_dtypes_and_shapes(L):
+    """The binding refuses, before any device work, scales whose element
+    width does not match scale_dtype (one byte for E8M0, float32 for F32),
+    non-byte operands, and a tile-scale tensor of the wrong shape."""
+    import torch
+    codes = torch.zeros(1, 8, 128, dtype=torch.uint8)
+    rcodes = torch.zeros(1, 16, 128, dtype=torch.uint8)
+    out = torch.zeros(1, 8, 16)
+    s8a = torch.zeros(1, 8, 4, dtype=torch.uint8)
+    s8b = torch.zeros(1, 16, 4, dtype=torch.uint8)
+    f32a = torch.zeros(1, 8, 1)
+    f32b = torch.zeros(1, 16, 1)
+    with pytest.raises(TypeError):   # float32 scales declared E8M0
+        bsq.bsq_scaled_matmul(codes, rcodes, f32a, f32b, out, scale_dtype=bsq.BSQ_E8M0)
+    with pytest.raises(TypeError):   # byte scales declared F32 (would be read 4x past their end)
+        bsq.bsq_scaled_matmul(codes, rcodes, s8a, s8b, out, scale_dtype=bsq.BSQ_F32)
+    with pytest.raises(TypeError):   # operands must be one byte per element
+        bsq.bsq_scaled_matmul(codes.float(), rcodes, s8a, s8b, out, scale_dtype=bsq.BSQ_E8M0)
+    src = torch.zeros(256, 256)
+    with pytest.raises(ValueError):  # [rows/128, cols/128] = [2, 2] expected
+        bsq.bsq_quant_fp8_tile(src, torch.zeros(256, 256, dtype=torch.uint8), torch.zeros(1, 2))
+    # correct dtypes and shapes get as far as the device check
+    with pytest.raises(ValueError, match="GPU"):
+        bsq.bsq_quant_fp8_tile(src, torch.zeros(256, 256, dtype=torch.uint8), torch.zeros(2, 2))
+    with pytest.raises(ValueError, match="GPU"):
+        bsq.bsq_scaled_matmul(codes, rcodes, s8a, s8b, out, scale_dtype=bsq.BSQ_E8M0)
