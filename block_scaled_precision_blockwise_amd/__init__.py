@@ -94,6 +94,11 @@ def lib() -> ctypes.CDLL:
     when the library has not been built."""
     global _lib
     if _lib is None:
+        # torch first: its HIP runtime (libamdhip64.so.7) is then already in
+        # the process and libbsq binds to that copy by soname.  Loading
+        # libbsq first would map ROCm's copy as well, and two HIP runtimes in
+        # one process do not share devices, streams or allocations.
+        _torch()
         if not is_built():
             raise RuntimeError(
                 f"libbsq.so not found at {_LIB_PATH}; build it with "

@@ -249,3 +249,16 @@ def test_binding_checks_scale_dtypes_and_shapes(L):
         bsq.bsq_quant_fp8_tile(src, torch.zeros(256, 256, dtype=torch.uint8), torch.zeros(2, 2))
     with pytest.raises(ValueError, match="GPU"):
         bsq.bsq_scaled_matmul(codes, rcodes, s8a, s8b, out, scale_dtype=bsq.BSQ_E8M0)
+
+
+def test_binding_loads_one_hip_runtime():
+    """Loading the library through the binding, before anything imported
+    torch, maps a single HIP runtime (torch's): libbsq binds to it by
+    soname instead of bringing a second copy."""
+    import subprocess
+    import sys
+    code = ("import block_scaled_precision_blockwise_amd as b; b.lib(); import torch; "
+            "print(len(set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l)))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1", r.stdout
