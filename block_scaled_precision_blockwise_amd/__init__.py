@@ -30,6 +30,7 @@ __all__ = [
     "bsq_int8_quant_rows", "bsq_int8_quant_cols",
     "bsq_blockwise_fp8_matmul", "bsq_scaled_matmul", "bsq_int8_matmul",
     "bsq_int8_workspace_bytes", "bsq_int8_per_channel_matmul",
+    "bsq_int8_noalloc_max_bytes", "bsq_int8_per_channel_matmul_noalloc",
     "bsq_mxfp8_backward_workspace_bytes", "bsq_mxfp8_backward",
     "mxfp8_backward_operand_shapes", "bsq_mxfp8_backward_quantize", "bsq_mxfp8_backward_gemms",
     "bsq_nvfp4_workspace_bytes", "bsq_scaled_matmul_nvfp4",
@@ -64,6 +65,8 @@ _SIGNATURES = {
     "bsq_int8_matmul": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "bsq_int8_workspace_bytes": (_SZ, [_I64, _I64]),
     "bsq_int8_per_channel_matmul": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "bsq_int8_noalloc_max_bytes": (_SZ, []),
+    "bsq_int8_per_channel_matmul_noalloc": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "bsq_mxfp8_backward_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "bsq_mxfp8_backward": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _INT, _P, _P, _P, _SZ, _P]),
     "bsq_mxfp8_backward_quantize": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, _P, _P,
@@ -378,6 +381,30 @@ def bsq_int8_per_channel_matmul(x, w, w_q, w_s, x_q, x_s, y, workspace, stream=N
     _raise(lib().bsq_int8_per_channel_matmul(B, D_in, D_out, _ptr(x), _ptr(w), _ptr(w_q), _ptr(w_s),
                                              _ptr(x_q), _ptr(x_s), _ptr(y), _ptr(workspace), nbytes,
                                              _stream(stream)), "bsq_int8_per_channel_matmul")
+
+
+def bsq_int8_noalloc_max_bytes() -> int:
+    return int(lib().bsq_int8_noalloc_max_bytes())
+
+
+def bsq_int8_per_channel_matmul_noalloc(x, w, w_q, w_s, x_q, x_s, y, stream=None):
+    """The int8 per-channel composite without a workspace (the library's
+    per-GPU scratch holds the transposed weight codes; D_in * D_out <=
+    bsq_int8_noalloc_max_bytes()).  Calls that overlap on one GPU race."""
+    torch = _torch()
+    _dev(x, w, w_q, w_s, x_q, x_s, y)
+    B, D_in = x.shape
+    D_out = w.shape[1]
+    _expect(x, torch.float32, (B, D_in), "x")
+    _expect(w, torch.float32, (D_in, D_out), "w")
+    _expect(w_q, torch.int8, (D_in, D_out), "w_q")
+    _expect(w_s, torch.float32, (D_out,), "w_s")
+    _expect(x_q, torch.int8, (B, D_in), "x_q")
+    _expect(x_s, torch.float32, (B,), "x_s")
+    _expect(y, torch.float32, (B, D_out), "y")
+    _raise(lib().bsq_int8_per_channel_matmul_noalloc(B, D_in, D_out, _ptr(x), _ptr(w), _ptr(w_q), _ptr(w_s),
+                                                     _ptr(x_q), _ptr(x_s), _ptr(y), _stream(stream)),
+           "bsq_int8_per_channel_matmul_noalloc")
 
 
 def bsq_mxfp8_backward_workspace_bytes(M: int, N: int, K: int) -> int:

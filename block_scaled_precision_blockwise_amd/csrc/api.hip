@@ -370,6 +370,89 @@ bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, c
   return bsq_int8_matmul(B, D_in, D_out, x_q, wqT, x_s, w_s, y, nullptr, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------- the composite, no allocation --
+// For callers that cannot allocate (HIP graph capture, tight serving loops,
+// harnesses that forbid hipMalloc): the int8 composite with its workspace
+// (the transposed weight codes) in a file-scope device array instead of a
+// caller buffer.  The array exists once per GPU for the life of the process;
+// host code never uses its name as an address, only the address that
+// hipGetSymbolAddress returns for the current device (each GPU holds its own
+// copy at its own address).
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;  // 16 MiB: D_in * D_out <= 2^24
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // per device: the address of `scratch`, or null before its first use
+
+// The current device's copy of `scratch`, looked up once per device with
+// that device current.
+bsq_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(BSQ_ERR_DEVICE, "no HIP device available");
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (size_t(dev) >= g_scratch_ptr.size()) g_scratch_ptr.resize(size_t(dev) + 1, nullptr);
+  if (g_scratch_ptr[size_t(dev)] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(BSQ_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    }
+    g_scratch_ptr[size_t(dev)] = ptr;
+  }
+  *out = g_scratch_ptr[size_t(dev)];
+  return BSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bsq_int8_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+bsq_status bsq_int8_per_channel_matmul_noalloc(int64_t B, int64_t D_in, int64_t D_out, const float* x,
+                                               const float* w, int8_t* w_q, float* w_s, int8_t* x_q,
+                                               float* x_s, float* y, void* stream) {
+  BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(D_in <= kMaxInt8Contraction, BSQ_ERR_UNSUPPORTED,
+            "D_in > 133144: int32 sums of int8 products could wrap");
+  const size_t need = bsq_int8_workspace_bytes(D_in, D_out);
+  BSQ_CHECK(need <= kNoAllocScratchBytes, BSQ_ERR_UNSUPPORTED,
+            "D_in * D_out exceeds the 16 MiB scratch of the no-allocation entry point");
+  // the composite's pointer rules, checked before the device is touched
+  if (B > 0) BSQ_CHECK_PTR(x_s);
+  if (B > 0 && D_in > 0) {
+    BSQ_CHECK_PTR(x);
+    BSQ_CHECK_PTR(x_q);
+  }
+  if (D_out > 0) BSQ_CHECK_PTR(w_s);
+  if (D_in > 0 && D_out > 0) {
+    BSQ_CHECK_PTR(w);
+    BSQ_CHECK_PTR(w_q);
+  }
+  if (B > 0 && D_out > 0) BSQ_CHECK_PTR(y);
+  void* ws = nullptr;
+  if (need > 0) {
+    BSQ_DEVICE();
+    const bsq_status s = scratch_for_current_device(&ws);
+    if (s != BSQ_OK) return s;
+  }
+  // the transposed codes are written in full by the column quantizer before
+  // the GEMM reads them: nothing in the scratch needs clearing
+  return bsq_int8_per_channel_matmul(B, D_in, D_out, x, w, w_q, w_s, x_q, x_s, y, ws, need, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
 // MXFP8 backward: four MX quantizations into the workspace, then two
 // scaled GEMMs on K-contiguous operands.
 namespace {

@@ -208,6 +208,23 @@ bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, c
                                        float* x_s, float* y, void* workspace,
                                        size_t workspace_bytes, void* stream);
 
+/* The same int8 composite for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument; the transposed weight codes go to a
+ * scratch array of bsq_int8_noalloc_max_bytes() bytes (16 MiB) that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates and frees nothing.  Outputs are identical to
+ * bsq_int8_per_channel_matmul's.
+ * Rules: as bsq_int8_per_channel_matmul, and D_in * D_out <= 2^24 (the
+ * scratch) else BSQ_ERR_UNSUPPORTED.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (e.g. on two
+ * streams) race and give undefined results; calls ordered on one stream do
+ * not. */
+size_t bsq_int8_noalloc_max_bytes(void);
+bsq_status bsq_int8_per_channel_matmul_noalloc(int64_t B, int64_t D_in, int64_t D_out, const float* x,
+                                               const float* w, int8_t* w_q, float* w_s, int8_t* x_q,
+                                               float* x_s, float* y, void* stream);
+
 /* MXFP8 linear-layer backward (mxfp8 backward: forward Y = X W^T with X
  * [M, K], W [N, K]; dX = dY W [M, K] contracting over N; dW = dY^T X [N, K]
  * contracting over M; bf16 inputs quantized on the fly).

@@ -251,6 +251,22 @@ def test_binding_checks_scale_dtypes_and_shapes(L):
         bsq.bsq_scaled_matmul(codes, rcodes, s8a, s8b, out, scale_dtype=bsq.BSQ_E8M0)
 
 
+def test_int8_noalloc_validation(L):
+    """The int8 composite without a workspace: its scratch is 16 MiB, larger
+    D_in * D_out and the int32 limit are refused, pointers are checked,
+    valid calls reach the device check."""
+    assert L.bsq_int8_noalloc_max_bytes() == 16 << 20
+    f = L.bsq_int8_per_channel_matmul_noalloc
+    args = [A16] * 7 + [None]
+    _expect(f(2, 4096, 4096, *args), DEVICE, L)              # exactly the scratch
+    _expect(f(2, 4096, 4112, *args), UNSUP, L)               # one row of the scratch too many
+    _expect(f(2, 133145, 16, *args), UNSUP, L)
+    _expect(f(-1, 64, 16, *args), SHAPE, L)
+    _expect(f(2, 64, 16, None, *([A16] * 6), None), NULL, L)
+    _expect(f(2, 64, 16, A16, A16, A16, A16, A16, A16, A4, None), ALIGN, L)
+    _expect(f(0, 0, 0, *([None] * 7), None), OK, L)
+
+
 def test_binding_loads_one_hip_runtime():
     """Loading the library through the binding, before anything imported
     torch, maps a single HIP runtime (torch's): libbsq binds to it by
