@@ -211,7 +211,7 @@ bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t gro
   BSQ_CHECK(known_dtype(out_dtype), BSQ_ERR_DTYPE, "unknown out_dtype");
   BSQ_CHECK(out_dtype == BSQ_F32 || out_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
             "out_dtype must be F32 or BF16");
-  BSQ_CHECK(group_k % 128 == 0, BSQ_ERR_UNSUPPORTED, "the library runs group_k multiples of 128");
+  BSQ_CHECK(group_k % 64 == 0, BSQ_ERR_UNSUPPORTED, "the library runs group_k multiples of 64");
   BSQ_CHECK(N % 16 == 0, BSQ_ERR_UNSUPPORTED, "N must be a multiple of 16");
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
@@ -233,12 +233,14 @@ bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t gro
   L.gn1 = group_n == 1;
   if (group_k != 128 || (group_n != 1 && group_n != 128)) {
     // general groups: per-column B scale rows n / group_n, group_k / 128
-    // K-steps per scale
+    // K-steps per scale (group_k / 64 half steps when group_k is not a
+    // multiple of 128)
     L.gen = true;
     L.gn1 = true;
     L.gn = int(group_n);
     L.sc_a = L.sc_b = int(K / group_k);
-    L.sg_a = L.sg_b = int(group_k / 128);
+    L.sub = group_k % 128 != 0;
+    L.sg_a = L.sg_b = int(group_k / (L.sub ? 64 : 128));
   }
   return launch_gemm(L, as_stream(stream));
 }
@@ -265,19 +267,21 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
   GemmLaunch L{};
   const int64_t blk_a = K / K_a, blk_b = K / K_b;  // elements per scale along K
   if (scale_dtype == BSQ_E8M0) {
-    BSQ_CHECK(blk_a % 32 == 0 && blk_b % 32 == 0, BSQ_ERR_UNSUPPORTED,
-              "E8M0 scale blocks must be multiples of 32");
+    BSQ_CHECK(blk_a % 16 == 0 && blk_b % 16 == 0, BSQ_ERR_UNSUPPORTED,
+              "E8M0 scale blocks must be multiples of 16");
     L.mode = MODE_MX;
     if (blk_a != 32 || blk_b != 32) {
       BSQ_CHECK(K_a % 4 == 0 && K_b % 4 == 0, BSQ_ERR_UNSUPPORTED,
                 "with E8M0 blocks other than 32, K_a and K_b must be multiples of 4");
       L.gen = true;
       L.sc_a = int(K_a); L.sc_b = int(K_b);
-      L.sg_a = int(blk_a / 32); L.sg_b = int(blk_b / 32);
+      // blocks that are not multiples of 32 count in 16-element granules
+      L.sub = blk_a % 32 != 0 || blk_b % 32 != 0;
+      L.sg_a = int(blk_a / (L.sub ? 16 : 32)); L.sg_b = int(blk_b / (L.sub ? 16 : 32));
     }
   } else if (scale_dtype == BSQ_F32) {
-    BSQ_CHECK(blk_a % 128 == 0 && blk_b % 128 == 0, BSQ_ERR_UNSUPPORTED,
-              "F32 scale blocks must be multiples of 128");
+    BSQ_CHECK(blk_a % 64 == 0 && blk_b % 64 == 0, BSQ_ERR_UNSUPPORTED,
+              "F32 scale blocks must be multiples of 64");
     BSQ_CHECK(lhs_dtype == BSQ_E4M3 && rhs_dtype == BSQ_E4M3, BSQ_ERR_UNSUPPORTED,
               "F32-scaled operands must be E4M3");
     L.mode = MODE_FP8G;
@@ -286,7 +290,9 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
       L.gen = true;
       L.gn = 1;
       L.sc_a = int(K_a); L.sc_b = int(K_b);
-      L.sg_a = int(blk_a / 128); L.sg_b = int(blk_b / 128);
+      // blocks that are not multiples of 128 count in 64-wide half steps
+      L.sub = blk_a % 128 != 0 || blk_b % 128 != 0;
+      L.sg_a = int(blk_a / (L.sub ? 64 : 128)); L.sg_b = int(blk_b / (L.sub ? 64 : 128));
     }
   } else {
     return fail(BSQ_ERR_UNSUPPORTED, "scale_dtype must be E8M0 or F32");

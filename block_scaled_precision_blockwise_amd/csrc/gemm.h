@@ -23,11 +23,13 @@ struct GemmLaunch {
   bool fa_e5m2, fb_e5m2;
   // General scale blocks (gen = true): SA [batch, M, sc_a], SB [batch, N /
   // gn (FP8G; gn a multiple of 128 takes one scale per 128 columns, others
-  // one per column) or N (MX), sc_b]; a scale covers sg_a / sg_b K-steps of 128
-  // (FP8G, float32 scales, e4m3 operands) or 32-element blocks (MX, e8m0);
-  // sc_a * sg_a * (128 or 32) == K, likewise for B; MX needs sc_a and sc_b
-  // multiples of 4 (word-aligned scale rows).
+  // one per column) or N (MX), sc_b]; a scale covers sg_a / sg_b granules:
+  // K-steps of 128 (FP8G, float32 scales, e4m3 operands) or 32-element
+  // blocks (MX, e8m0); with sub = true, half steps of 64 (FP8G) or
+  // 16-element blocks (MX).  sc_a * sg_a * granule == K, likewise for B; MX
+  // needs sc_a and sc_b multiples of 4 (word-aligned scale rows).
   bool gen;
+  bool sub;
   int sc_a, sc_b, sg_a, sg_b, gn;
 };
 

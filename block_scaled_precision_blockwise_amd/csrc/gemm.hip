@@ -238,11 +238,17 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const acc_t (&acc)
 // (Measured alternatives that were not faster: 4 waves of 128 x 128 with
 // AGPR accumulators; two wave groups alternating between MFMA and memory
 // phases with a barrier per phase; an L2 prefetch two steps ahead.)
-template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM, int GEN = 0>
+// SUB (general blocks only): scale blocks shorter than the MFMA's K - FP8G
+// float32 blocks that are multiples of 64 (not of 128), E8M0 blocks that
+// are multiples of 16 (not of 32).  Each block then takes two MFMAs per
+// K-step, each with part of the A fragment zeroed so that it sums exactly
+// one sub-block of every 128-wide step (see the loop).
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int NW, int TBM, int GEN = 0, int SUB = 0>
 __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   static_assert(NW == 8, "8 waves: the wave layout, scale staging and epilogue assume it");
   static_assert(TBM == 256 || TBM == 192 || TBM == 128, "tile rows");
   static_assert(!GEN || MODE == MODE_FP8G || MODE == MODE_MX, "general blocks: FP8G or MX");
+  static_assert(!SUB || GEN, "sub-step blocks go through the general scale staging");
   constexpr int NT = 64 * NW;          // threads
   constexpr int WGM = 4;                // waves along M
   constexpr int MB = TBM / WGM / 16;    // 16-row blocks per wave along M
@@ -255,10 +261,16 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_ab[kLdsAB];
   uint8_t* const lds_a = lds_ab;                 // stage st at + st * TBM * BK
   uint8_t* const lds_b = lds_ab + 2 * TBM * BK;  // stage st at + st * BN * BK
-  // scales of kSG consecutive K-steps: slot r < 256 holds A row r, slot
-  // 256 + r B row r (MX, FP8G with GN1) or B row group r (FP8G); the word of
-  // step ks sits at [(ks / kSG) & 1][slot * kSG + ks % kSG]
+  // scales of kGS consecutive K-steps, kSG words (16 bytes) per slot: slot
+  // r < 256 holds A row r, slot 256 + r B row r (MX, FP8G with GN1) or B
+  // row group r (FP8G); without general blocks the word of step ks sits at
+  // [(ks / kSG) & 1][slot * kSG + ks % kSG].  General blocks: a slot's 16
+  // bytes start at the first scale of the group (the granule index - 128,
+  // or 64 for SUB, K-wide steps for FP8G; 32-, or 16-element blocks for MX -
+  // of the group's first granule, over granules per scale); a group is 4
+  // steps, 2 for SUB, so that it spans at most 16 bytes of scales.
   constexpr int kSG = 4;
+  constexpr int kGS = SUB ? 2 : 4;
   __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][512 * kSG];
 
   const int tid = threadIdx.x;
@@ -415,8 +427,8 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     const int st = ks & 1;
     const int kn = ks + 1;
     // the next group's scales during the last step of this group (the
-    // buffer they go to was last read kSG steps ago)
-    if (ks % kSG == kSG - 1 && ks + 1 < nk) sload((ks + 1) / kSG);
+    // buffer they go to was last read kGS steps ago)
+    if (ks % kGS == kGS - 1 && ks + 1 < nk) sload((ks + 1) / kGS);
 
     const uint8_t* ta = lds_a + st * TBM * BK;
     const uint8_t* tb = lds_b + st * BN * BK;
@@ -426,15 +438,33 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
     const uint32_t* ssa = ss;
     const uint32_t* ssb = ss;
     int mxa = 0, mxb = 0;
+    // SUB: the word (FP8G) / byte (MX) of the second sub-block of the step
+    // (FP8G: K 64..127; MX: the second 16 elements of the lane's 32-block)
+    const uint32_t* ssa1 = ss;
+    const uint32_t* ssb1 = ss;
+    int mxa1 = 0, mxb1 = 0;
     if (GEN) {
-      const int q = ks / kSG;
+      const int q = ks / kGS;
       if (MODE == MODE_FP8G) {
-        ssa = &lds_s[q & 1][ks / p.sg_a - (kSG * q) / p.sg_a];
-        ssb = &lds_s[q & 1][ks / p.sg_b - (kSG * q) / p.sg_b];
+        // granule = K-step (64-wide half step for SUB); 4 granules per group
+        const int gr0 = SUB ? 2 * ks : ks;
+        ssa = &lds_s[q & 1][gr0 / p.sg_a - (4 * q) / p.sg_a];
+        ssb = &lds_s[q & 1][gr0 / p.sg_b - (4 * q) / p.sg_b];
+        if (SUB) {
+          ssa1 = &lds_s[q & 1][(gr0 + 1) / p.sg_a - (4 * q) / p.sg_a];
+          ssb1 = &lds_s[q & 1][(gr0 + 1) / p.sg_b - (4 * q) / p.sg_b];
+        }
       } else {
-        ssa = ssb = &lds_s[q & 1][0];
-        mxa = (4 * ks + g) / p.sg_a - (((16 * q) / p.sg_a) & ~3);
-        mxb = (4 * ks + g) / p.sg_b - (((16 * q) / p.sg_b) & ~3);
+        // granule = the lane's 32-element block (16-element sub-block for
+        // SUB); 16 granules per group
+        ssa = ssb = ssa1 = ssb1 = &lds_s[q & 1][0];
+        const int gr0 = SUB ? 8 * ks + 2 * g : 4 * ks + g;
+        mxa = gr0 / p.sg_a - (((16 * q) / p.sg_a) & ~3);
+        mxb = gr0 / p.sg_b - (((16 * q) / p.sg_b) & ~3);
+        if (SUB) {
+          mxa1 = (gr0 + 1) / p.sg_a - (((16 * q) / p.sg_a) & ~3);
+          mxb1 = (gr0 + 1) / p.sg_b - (((16 * q) / p.sg_b) & ~3);
+        }
       }
     }
     // LDS reads retire in order, so a wait for one read also waits for all
@@ -450,21 +480,30 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       const int rowb = 128 * wn + 16 * j + r16;
       return lds_frag(tb, rowb * BK + c0, rowb * BK + c1);
     };
-    float sa[MB];
-    uint32_t qa_w[MB], qb_w[NB];
-    float sbg = 0.f;
+    float sa[MB], sa1[MB];
+    uint32_t qa_w[MB], qb_w[NB], qa_w1[MB];
+    float sbg = 0.f, sbg1 = 0.f;
     if (MODE == MODE_FP8G) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) sa[i] = __uint_as_float(ssa[(16 * MB * wm + 16 * i + r16) * kSG]);
       if (!GN1) sbg = __uint_as_float(ssb[(256 + wn) * kSG]);
+      if (SUB) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) sa1[i] = __uint_as_float(ssa1[(16 * MB * wm + 16 * i + r16) * kSG]);
+        if (!GN1) sbg1 = __uint_as_float(ssb1[(256 + wn) * kSG]);
+      }
     } else if (MODE == MODE_MX) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) qa_w[i] = ssa[(16 * MB * wm + 16 * i + r16) * kSG + (GEN ? mxa >> 2 : 0)];
 #pragma unroll
       for (int j = 0; j < NB; ++j) qb_w[j] = ssb[(256 + 128 * wn + 16 * j + r16) * kSG + (GEN ? mxb >> 2 : 0)];
+      if (SUB) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i) qa_w1[i] = ssa1[(16 * MB * wm + 16 * i + r16) * kSG + (mxa1 >> 2)];
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the scale reads ahead of the fragment reads
-    constexpr int PF = 2;  // B fragments in flight ahead of their MFMAs
+    constexpr int PF = SUB ? 1 : 2;  // B fragments in flight ahead of their MFMAs
     v8i pq[PF];
     pq[0] = bfrag(0);
     v8i q[MB];
@@ -495,7 +534,53 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       v8i pnext;
       if (j + PF < NB) pnext = bfrag(j + PF);
       const v8i pb = pq[0];
-      if (MODE == MODE_FP8G) {
+      if (SUB && MODE == MODE_FP8G) {
+        // two 64-wide K groups per step: a lane's first 16 fragment bytes
+        // hold K 16g..16g+15 (< 64), its last 16 K 64+16g.. (>= 64), so
+        // zeroing one half of the A fragment leaves exactly one group's
+        // products; each partial takes its own pair of scales
+        float sl[4] = {0.f, 0.f, 0.f, 0.f}, sh[4] = {0.f, 0.f, 0.f, 0.f};
+        if (GN1) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sl[r] = __uint_as_float(ssb[(256 + 128 * wn + 16 * j + 4 * g + r) * kSG]);
+            sh[r] = __uint_as_float(ssb1[(256 + 128 * wn + 16 * j + 4 * g + r) * kSG]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const v4f zero = {0.f, 0.f, 0.f, 0.f};
+          const v8i qlo = {q[i][0], q[i][1], q[i][2], q[i][3], 0, 0, 0, 0};
+          const v8i qhi = {0, 0, 0, 0, q[i][4], q[i][5], q[i][6], q[i][7]};
+          const v4f dl = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, qlo, zero, 0, 0, 0, 0, 0, 0);
+          const v4f dh = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, qhi, zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float fl = GN1 ? sa[i] * sl[r] : sa[i] * sbg;
+            const float fh = GN1 ? sa1[i] * sh[r] : sa1[i] * sbg1;
+            acc[j][i][r] = fmaf(dh[r], fh, fmaf(dl[r], fl, acc[j][i][r]));
+          }
+        }
+      } else if (SUB && MODE == MODE_MX) {
+        // 16-element blocks: a lane's fragment holds the first halves of its
+        // two 32-blocks when g is even, the second halves when g is odd.
+        // MFMA h keeps the lanes with g % 2 == h (the others' A bytes are
+        // zeroed) and takes the scales of those halves.
+        const uint32_t qbw1 = ssb1[(256 + 128 * wn + 16 * j + r16) * kSG + (mxb1 >> 2)];
+        const int qb0 = int((qb_w[j] >> (8 * (mxb & 3))) & 0xFFu);
+        const int qb1 = int((qbw1 >> (8 * (mxb1 & 3))) & 0xFFu);
+        const bool odd = (g & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
+          const v8i q0 = odd ? z : q[i];
+          const v8i q1 = odd ? q[i] : z;
+          const int qa0 = int((qa_w[i] >> (8 * (mxa & 3))) & 0xFFu);
+          const int qa1 = int((qa_w1[i] >> (8 * (mxa1 & 3))) & 0xFFu);
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q0, acc[j][i], FB, FA, 0, qb0, 0, qa0);
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q1, acc[j][i], FB, FA, 0, qb1, 0, qa1);
+        }
+      } else if (MODE == MODE_FP8G) {
         float sb4[4] = {0.f, 0.f, 0.f, 0.f};
         if (GN1) {
 #pragma unroll
@@ -550,7 +635,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t + 1 < PF; ++t) pq[t] = pq[t + 1];
       if (j + PF < NB) pq[PF - 1] = pnext;
-      if (MODE == MODE_FP8G && j > 0) {
+      if (MODE == MODE_FP8G && !SUB && j > 0) {
         // issue order: the two prefetch reads, then one MFMA followed by
         // four rescale FMAs, MB times
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -562,7 +647,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (MODE == MODE_FP8G) rescale(NB - 1, dprev, sb4p);
+    if (MODE == MODE_FP8G && !SUB) rescale(NB - 1, dprev, sb4p);
 
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
@@ -837,13 +922,13 @@ void launch_gemm_kernel(Kernel k, dim3 grid, dim3 block, hipStream_t st, Args...
     hipLaunchKernelGGL(k, grid, block, 0, st, args...);
 }
 
-template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int GEN = 0>
+template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int GEN = 0, int SUB = 0>
 bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   const int64_t tiles = int64_t((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * batch;
   if constexpr (GEN != 0) {
     // general scale blocks: the big-tile kernel at every size
     dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
-    launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1>, grid, dim3(512), st, a);
+    launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1, SUB>, grid, dim3(512), st, a);
     return launch_status("gemm (general scale blocks)");
   }
   if constexpr (MODE != MODE_BF16) {
@@ -923,16 +1008,34 @@ bsq_status launch_gemm(const GemmLaunch& L, hipStream_t st) {
   if (L.gen && L.mode == MODE_FP8G) {
     a.sSA = L.M * L.sc_a;
     a.sSB = (L.N / L.gn) * L.sc_b;
-    if (L.gn % 128 == 0)  // one B scale per wave's 128 columns
-      return L.out_bf16 ? run<MODE_FP8G, 1, 0, 0, 0, 1>(a, int(L.batch), st)
-                        : run<MODE_FP8G, 0, 0, 0, 0, 1>(a, int(L.batch), st);
-    return L.out_bf16 ? run<MODE_FP8G, 1, 0, 0, 1, 1>(a, int(L.batch), st)
-                      : run<MODE_FP8G, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+    const int sel = (L.gn % 128 == 0 ? 0 : 1) | (L.out_bf16 ? 2 : 0) | (L.sub ? 4 : 0);
+    switch (sel) {  // gn % 128 == 0: one B scale per wave's 128 columns
+      case 0: return run<MODE_FP8G, 0, 0, 0, 0, 1>(a, int(L.batch), st);
+      case 1: return run<MODE_FP8G, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+      case 2: return run<MODE_FP8G, 1, 0, 0, 0, 1>(a, int(L.batch), st);
+      case 3: return run<MODE_FP8G, 1, 0, 0, 1, 1>(a, int(L.batch), st);
+      case 4: return run<MODE_FP8G, 0, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+      case 5: return run<MODE_FP8G, 0, 0, 0, 1, 1, 1>(a, int(L.batch), st);
+      case 6: return run<MODE_FP8G, 1, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+      default: return run<MODE_FP8G, 1, 0, 0, 1, 1, 1>(a, int(L.batch), st);
+    }
   }
   if (L.gen && L.mode == MODE_MX) {
     a.sSA = L.M * L.sc_a;
     a.sSB = L.N * L.sc_b;
     const int sel = (L.fa_e5m2 ? 1 : 0) | (L.fb_e5m2 ? 2 : 0) | (L.out_bf16 ? 4 : 0);
+    if (L.sub) {
+      switch (sel) {
+        case 0: return run<MODE_MX, 0, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+        case 1: return run<MODE_MX, 0, 1, 0, 0, 1, 1>(a, int(L.batch), st);
+        case 2: return run<MODE_MX, 0, 0, 1, 0, 1, 1>(a, int(L.batch), st);
+        case 3: return run<MODE_MX, 0, 1, 1, 0, 1, 1>(a, int(L.batch), st);
+        case 4: return run<MODE_MX, 1, 0, 0, 0, 1, 1>(a, int(L.batch), st);
+        case 5: return run<MODE_MX, 1, 1, 0, 0, 1, 1>(a, int(L.batch), st);
+        case 6: return run<MODE_MX, 1, 0, 1, 0, 1, 1>(a, int(L.batch), st);
+        default: return run<MODE_MX, 1, 1, 1, 0, 1, 1>(a, int(L.batch), st);
+      }
+    }
     switch (sel) {
       case 0: return run<MODE_MX, 0, 0, 0, 0, 1>(a, int(L.batch), st);
       case 1: return run<MODE_MX, 0, 1, 0, 0, 1>(a, int(L.batch), st);

@@ -155,10 +155,12 @@ bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8
  *   b_scales float32 [N / group_n, K / group_k]
  *   out      [M, N], out_dtype BSQ_F32 or BSQ_BF16 (nearest even)
  * Rules: N % group_n == 0, K % group_k == 0; M >= 0 arbitrary.  The library
- * runs any group_n (N % 16 == 0) and group_k a multiple of 128; other
- * group_k -> UNSUPPORTED.  group_k == 128 with group_n 1 or 128 is the
- * tuned kernel; other groups run the same kernel with general scale
- * indexing (slower scale handling). */
+ * runs any group_n (N % 16 == 0) and group_k a multiple of 64 with K % 128
+ * == 0; other group_k -> UNSUPPORTED.  group_k == 128 with group_n 1 or
+ * 128 is the tuned kernel; other groups run the same kernel with general
+ * scale indexing (slower scale handling), and a group_k that is not a
+ * multiple of 128 takes two matrix-core products per 128-wide K-step
+ * (about half the rate). */
 bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t group_n,
                                     int64_t group_k, const uint8_t* a, const uint8_t* b,
                                     const float* a_scales, const float* b_scales, void* out,
@@ -172,10 +174,12 @@ bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t gro
  *   out [B, M, N] of out_dtype (BSQ_F32, the page's default, or BSQ_BF16)
  * Rules: K % K_a == 0 and K % K_b == 0 (else SHAPE).  The library runs
  * (K % 128 == 0, N % 16 == 0): scale_dtype E8M0 with blocks K / K_a and
- * K / K_b multiples of 32 (they may differ; unless both are 32, K_a and
+ * K / K_b multiples of 16 (they may differ; unless both are 32, K_a and
  * K_b must be multiples of 4); scale_dtype F32 with E4M3 operands and
- * blocks multiples of 128 (may differ).  Other valid combinations (e.g.
- * block 16) -> UNSUPPORTED. */
+ * blocks multiples of 64 (may differ).  Blocks that are not multiples of
+ * 32 (E8M0) or 128 (F32) take two matrix-core products per 128-wide
+ * K-step (about half the rate).  Other valid combinations (e.g. E8M0
+ * block 8) -> UNSUPPORTED. */
 bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t K_a,
                              int64_t K_b, const void* lhs, int lhs_dtype, const void* rhs,
                              int rhs_dtype, const void* lhs_scales, const void* rhs_scales,

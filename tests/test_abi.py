@@ -84,7 +84,9 @@ def test_blockwise_validation(L):
     args = (A16, A16, A16, A16, A16, bsq.BSQ_F32, None)
     _expect(f(16, 256, 200, 128, 128, *args), SHAPE, L)        # K % group_k
     _expect(f(16, 200, 256, 128, 128, *args), SHAPE, L)        # N % group_n
-    _expect(f(16, 256, 256, 128, 64, *args), UNSUP, L)         # group_k 64
+    _expect(f(16, 256, 256, 128, 32, *args), UNSUP, L)         # group_k 32
+    _expect(f(16, 256, 256, 128, 64, *args), DEVICE, L)        # group_k 64 (two products per step)
+    _expect(f(16, 256, 384, 128, 192, *args), DEVICE, L)       # group_k 192
     _expect(f(16, 256, 512, 64, 256, *args), DEVICE, L)        # group_n 64, group_k 256
     _expect(f(16, 240, 384, 48, 384, *args), DEVICE, L)        # group_n 48, group_k 384
     _expect(f(16, 256, 256, 128, 128, A16, A16, A16, A16, A16, bsq.BSQ_I8, None), UNSUP, L)
@@ -99,8 +101,11 @@ def test_scaled_matmul_validation(L):
     E4, E5, E8, F32 = bsq.BSQ_E4M3, bsq.BSQ_E5M2, bsq.BSQ_E8M0, bsq.BSQ_F32
     # K % K_a != 0 is a shape error (the page's rule)
     _expect(f(1, 8, 16, 128, 3, 4, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), SHAPE, L)
-    # valid but not run here: block 16 e8m0, or an int8 operand
-    _expect(f(1, 8, 16, 128, 8, 8, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
+    # valid but not run here: block 8 e8m0, or an int8 operand
+    _expect(f(1, 8, 16, 128, 16, 16, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
+    # e8m0 block 16 (two products per step), alone or beside block 32
+    _expect(f(1, 8, 16, 128, 8, 8, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), DEVICE, L)
+    _expect(f(1, 8, 16, 128, 8, 4, A16, E4, A16, E5, A16, A16, E8, A16, F32, None), DEVICE, L)
     _expect(f(1, 8, 16, 128, 4, 4, A16, bsq.BSQ_I8, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
     _expect(f(1, 8, 16, 128, 4, 4, A16, E4, A16, E5, A16, A16, E8, A16, F32, None), DEVICE, L)
     _expect(f(1, 8, 16, 256, 2, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), DEVICE, L)
@@ -111,7 +116,8 @@ def test_scaled_matmul_validation(L):
     _expect(f(1, 8, 16, 512, 8, 16, A16, E4, A16, E5, A16, A16, E8, A16, F32, None), DEVICE, L)
     _expect(f(1, 8, 16, 256, 2, 8, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
     _expect(f(1, 8, 16, 768, 3, 6, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), DEVICE, L)
-    _expect(f(1, 8, 16, 256, 4, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), UNSUP, L)
+    _expect(f(1, 8, 16, 256, 4, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), DEVICE, L)  # F32 block 64
+    _expect(f(1, 8, 16, 256, 8, 2, A16, E4, A16, E4, A16, A16, F32, A16, F32, None), UNSUP, L)   # F32 block 32
 
 
 def test_int8_validation(L):

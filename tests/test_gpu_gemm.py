@@ -297,7 +297,10 @@ def test_blockwise_group_n_1_via_scaled_matmul_f32():
 
 @pytest.mark.parametrize("M,N,K,gn,gk", [(300, 384, 768, 64, 256), (257, 240, 1152, 48, 384),
                                          (513, 512, 1024, 256, 512), (130, 272, 640, 16, 128),
-                                         (200, 256, 512, 1, 256), (200, 384, 512, 128, 256)])
+                                         (200, 256, 512, 1, 256), (200, 384, 512, 128, 256),
+                                         # group_k below the matrix core's 128: two products per step
+                                         (300, 384, 640, 128, 64), (257, 240, 1152, 48, 192),
+                                         (130, 272, 384, 16, 64), (513, 256, 256, 1, 64)])
 def test_blockwise_general_groups(M, N, K, gn, gk):
     torch = _torch()
     say("blockwise general groups", M, N, K, gn, gk)
@@ -334,9 +337,14 @@ def test_blockwise_general_groups_full_size_sampled():
     (2, 100, 272, 512, 64, 32, "e4m3", "e5m2", "f32"),
     (2, 130, 144, 1024, 128, 256, "e5m2", "e5m2", "bf16"),
     (1, 64, 64, 768, 96, 64, "e4m3", "e4m3", "f32"),
+    # blocks of 16 (and 48): two products per step, alone and beside 32
+    (2, 100, 272, 512, 16, 32, "e4m3", "e5m2", "f32"),
+    (1, 130, 144, 256, 16, 16, "e5m2", "e5m2", "bf16"),
+    (2, 64, 64, 384, 48, 16, "e4m3", "e4m3", "f32"),
+    (1, 300, 512, 512, 32, 16, "e4m3", "e4m3", "f32"),
 ])
 def test_scaled_matmul_e8m0_general_blocks(Bt, M, N, K, ba, bb, lf, rf, out):
-    """E8M0 scales with blocks K / K_a != K / K_b (multiples of 32)."""
+    """E8M0 scales with blocks K / K_a != K / K_b (multiples of 16)."""
     torch = _torch()
     say("scaled_matmul e8m0 blocks", Bt, M, N, K, ba, bb)
     a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 810 + ba), lf)
@@ -353,9 +361,12 @@ def test_scaled_matmul_e8m0_general_blocks(Bt, M, N, K, ba, bb, lf, rf, out):
     assert_within_T(yh, yr, T, "y", bf16=(out == "bf16"))
 
 
-@pytest.mark.parametrize("Bt,M,N,K,ba,bb", [(2, 70, 144, 768, 256, 128), (1, 100, 256, 1536, 384, 512)])
+@pytest.mark.parametrize("Bt,M,N,K,ba,bb", [(2, 70, 144, 768, 256, 128), (1, 100, 256, 1536, 384, 512),
+                                             # blocks of 64 and 192: two products per step
+                                             (2, 70, 144, 768, 64, 128), (1, 100, 256, 1536, 192, 64),
+                                             (1, 260, 128, 384, 64, 64)])
 def test_scaled_matmul_f32_general_blocks(Bt, M, N, K, ba, bb):
-    """float32 scales with blocks K / K_a != K / K_b (multiples of 128)."""
+    """float32 scales with blocks K / K_a != K / K_b (multiples of 64)."""
     torch = _torch()
     say("scaled_matmul f32 blocks", Bt, M, N, K, ba, bb)
     a, _ = OQ.fp8_rowblock(synth.randn_f32((Bt * M, K), 820 + ba))

@@ -95,6 +95,53 @@ def test_blockwise_general_groups_recipe_operands_strict_sampled():
     assert np.all(np.isfinite(yh)), "unwritten output"
 
 
+def test_blockwise_group_k_64_recipe_operands_strict_sampled():
+    """m = n = k = 4096 with group_k 64 (below the matrix core's 128-wide
+    K: two products per step), operands from the recipe at that group (1 x
+    64 activation blocks, 128 x 64 weight tiles): sampled rows within
+    1e-4 T, float32 and bfloat16 out."""
+    torch = _torch()
+    M = N = K = 4096
+    gn, gk = 128, 64
+    say("blockwise group_k 64 recipe strict", M, N, K, gn, gk)
+    a32, b32 = synth.fp8_blockwise_raw(M, N, K, 1330, 1331)
+    a, sa = OQ.fp8_rowblock(a32, gk)
+    b, sb = OQ.fp8_tile(b32, gn, gk)
+    del a32, b32
+    rows = _rows_sample(M, seed=17)
+    yr, T = OM.blockwise_fp8(a[rows], b, sa[rows], sb, group_n=gn, group_k=gk)
+    da, db, dsa, dsb = to_dev(a), to_dev(b), to_dev(sa), to_dev(sb)
+    for od in (torch.float32, torch.bfloat16):
+        y = filled((M, N), od, float("nan"))
+        bsq.bsq_blockwise_fp8_matmul(da, db, dsa, dsb, y, group_n=gn, group_k=gk)
+        yh = host(y)
+        yv = yh[rows] if od == torch.float32 else OF.decode_bf16(yh[rows])
+        assert_within_T(yv, yr, T, f"y rows ({od})", bf16=(od == torch.bfloat16))
+        if od == torch.float32:
+            assert np.all(np.isfinite(yh)), "unwritten output"
+
+
+def test_scaled_matmul_e8m0_block_16_sampled():
+    """MX with E8M0 blocks of 16 (scaled_matmul: any block dividing K) at B =
+    2, 1024 x 2048 x 2048: the quantizer's e4m3 codes of randn with random
+    exponents per 16-element block, sampled rows within 1e-4 T."""
+    torch = _torch()
+    Bt, M, N, K = 2, 1024, 2048, 2048
+    say("scaled_matmul e8m0 block 16", Bt, M, N, K)
+    a, _ = OQ.mx(synth.randn_f32((Bt, M, K), 1340), "e4m3")
+    b, _ = OQ.mx(synth.randn_f32((Bt, N, K), 1341), "e4m3")
+    sa = synth.random_e8m0_codes((Bt, M, K // 16), 1342)
+    sb = synth.random_e8m0_codes((Bt, N, K // 16), 1343)
+    y = filled((Bt, M, N), torch.float32, float("nan"))
+    bsq.bsq_scaled_matmul(to_dev(a), to_dev(b), to_dev(sa), to_dev(sb), y, lhs_dtype=bsq.BSQ_E4M3,
+                          rhs_dtype=bsq.BSQ_E4M3, scale_dtype=bsq.BSQ_E8M0)
+    yh = host(y)
+    rows = _rows_sample(M, n=24, seed=19)
+    yr, T = OM.scaled_matmul(a[:, rows], b, sa[:, rows], sb, "e4m3", "e4m3", "e8m0")
+    assert_within_T(yh[:, rows], yr, T, "y rows")
+    assert np.all(np.isfinite(yh)), "unwritten output"
+
+
 # --------------------------------------------- the matrix core's groups ---
 
 E4_448 = 0x7E          # 448
