@@ -469,7 +469,7 @@ def run_suite(args):
     a = torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev)
     b = torch.randint(0, 126, (N, K), dtype=torch.uint8, device=dev)
     y = torch.empty(M, N, dtype=torch.float32, device=dev)
-    for gn, gk in ((128, 256), (64, 128)):
+    for gn, gk in ((128, 256), (64, 128), (128, 64)):
         sa = torch.rand(M, K // gk, device=dev)
         sb = torch.rand(N // gn, K // gk, device=dev)
         ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(a, b, sa, sb, y, group_n=gn, group_k=gk), 20)
@@ -536,6 +536,14 @@ def run_suite(args):
                                                        scale_dtype=bsq.BSQ_E8M0), 10)
     mfma_row("gemm_mx_batched", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/64 f32 out", ms, 2 * Bt * M * N * K,
              PEAK_FP8_TFLOPS)
+    sa16 = torch.randint(124, 131, (Bt, M, K // 16), dtype=torch.uint8, device=dev)
+    sb16 = torch.randint(124, 131, (Bt, N, K // 16), dtype=torch.uint8, device=dev)
+    ms = time_launches(lambda i: bsq.bsq_scaled_matmul(lq.view(Bt, M, K), rq.view(Bt, N, K), sa16, sb16, ym,
+                                                       lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3,
+                                                       scale_dtype=bsq.BSQ_E8M0), 10)
+    mfma_row("gemm_mx_batched", f"B={Bt} {M}x{N}x{K} e4m3 e8m0/16 f32 out (two products per step)", ms,
+             2 * Bt * M * N * K, PEAK_FP8_TFLOPS)
+    del sa16, sb16
     del lhs32, ls
     # cold: 4 operand sets (512 MiB of codes) rotated
     mops = [(lq.view(Bt, M, K), rq.view(Bt, N, K))] + [
