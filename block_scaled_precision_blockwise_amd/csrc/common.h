@@ -44,37 +44,6 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // -------------------------------------------------- device arithmetic ----
 
-// OCP fp8 encode of a finite float32 with |v| <= the format's maximum,
-// round to nearest with ties to even, sign kept (so -0 -> 0x80).
-// MBITS / BIAS: e4m3fn = 3 / 7, e5m2 = 2 / 15.  Integer rounding of the
-// float32 mantissa for normal results; for results below the smallest
-// normal the value is scaled to units of the smallest subnormal (exact: a
-// power of two) and rounded with v_rndne.
-template <int MBITS, int BIAS>
-__device__ __forceinline__ uint32_t encode_fp8(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  const float af = __uint_as_float(a);
-  // smallest normal of the format: 2^(1 - BIAS)
-  const float min_normal = __uint_as_float(uint32_t(127 + 1 - BIAS) << 23);
-  // 2^(BIAS - 1 + MBITS): one unit = the smallest subnormal
-  const float sub_unit = __uint_as_float(uint32_t(127 + BIAS - 1 + MBITS) << 23);
-  uint32_t code;
-  if (af < min_normal) {
-    code = uint32_t(__builtin_rintf(af * sub_unit));
-  } else {
-    const uint32_t drop = 23 - MBITS;
-    const uint32_t lsb = (a >> drop) & 1u;
-    const uint32_t r = (a + ((1u << (drop - 1)) - 1u) + lsb) >> drop;
-    code = r - (uint32_t(127 - BIAS) << MBITS);
-  }
-  return code | sign;
-}
-
-__device__ __forceinline__ uint32_t encode_e4m3(float v) { return encode_fp8<3, 7>(v); }
-__device__ __forceinline__ uint32_t encode_e5m2(float v) { return encode_fp8<2, 15>(v); }
-
 // float32 -> bfloat16 bits, nearest with ties to even (finite inputs).
 __device__ __forceinline__ uint32_t encode_bf16(float v) {
   const uint32_t u = __float_as_uint(v);

@@ -23,6 +23,15 @@
 // with few tiles run k_gemm_sk instead (64 x 64 tiles, K split over the
 // workgroup's waves).
 //
+// Unscaled products (FP8G, and the I8/BF16 modes' own instructions): the
+// FP8G calls go through the scaled builtin with all four scale operands
+// (format selectors and E8M0 bytes) zero; for constant zero scale operands
+// the compiler emits the plain v_mfma_f32_16x16x128_f8f6f4, which applies
+// no block scale (the FP8G kernels' code holds no v_mfma_scale or
+// v_mfma_ld_scale instruction).  Were a scaled form emitted instead, a zero
+// E8M0 byte would mean 2^-127 per operand and every FP8G product would
+// vanish, which each FP8G parity test would catch.
+//
 // Fragment layout (measured on gfx950): for the 16x16x128 f8 MFMA a lane
 // l supplies 32 bytes of row l % 16: K [16g, 16g+16) in bytes 0..15 and K
 // [64+16g, 64+16g+16) in bytes 16..31, g = l / 16; its E8M0 scale covers
@@ -552,6 +561,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
           const v8i qlo = {q[i][0], q[i][1], q[i][2], q[i][3], 0, 0, 0, 0};
           const v8i qhi = {0, 0, 0, 0, q[i][4], q[i][5], q[i][6], q[i][7]};
+          // zero scale operands: the unscaled MFMA (see the file header)
           const v4f dl = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, qlo, zero, 0, 0, 0, 0, 0, 0);
           const v4f dh = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, qhi, zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
@@ -590,6 +600,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
+          // zero scale operands: the unscaled MFMA (see the file header)
           dcur[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(pb, q[i], zero, 0, 0, 0, 0, 0, 0);
         }
         if (j > 0) rescale(j - 1, dprev, sb4p);
@@ -792,6 +803,7 @@ __global__ void __launch_bounds__(64 * SKW, 8 / SKW) k_gemm_sk(GemmArgs p) {
         for (int i = 0; i < 4; ++i) {
           if (MODE == MODE_FP8G) {
             const v4f zero = {0.f, 0.f, 0.f, 0.f};
+            // zero scale operands: the unscaled MFMA (see the file header)
             const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur[4 + j], cur[i], zero, 0, 0, 0, 0, 0, 0);
             const float sc = sa[i] * sb;
 #pragma unroll
