@@ -23,6 +23,14 @@ times every kernel of the path at its own workload (quantizers, FP8 GEMM
 sweep, INT8 per-channel, MXFP8 batched, MXFP8 backward) and writes one JSON
 object per kernel to FILE (default bench_out/suite.jsonl).
 
+    python bench.py --sweep [--out FILE]
+runs the GEMM on every row of the block_scaled_mm page's shape table.
+
+    python bench.py --operand-sweep [--steps K] [--warmup W] [--out FILE]
+times the 4096^3 GEMM on operands of different value patterns (the recipe's
+codes, uniform random codes, zeros, a constant, mostly zeros): same
+instructions, different clock.
+
 One GPU only: --gpus N with N > 1 exits with a message.
 """
 from __future__ import annotations
@@ -668,6 +676,87 @@ def run_sweep(args):
         torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------- operand sweep ---
+
+OPERAND_SETS = ("recipe", "uniform", "zero", "constant", "sparse")
+
+
+def run_operand_sweep(args):
+    """The 4096^3 group-128 GEMM on operands of different value patterns,
+    with the same scales: the recipe's (randn quantized 1 x 128 and
+    128 x 128, as in the main step), uniform random e4m3 codes, all-zero
+    codes, one constant code (1.0), and random codes of which 7 in 8 are
+    zero.  The kernel's instruction stream does not depend on the values,
+    so a difference in time is a difference in clock: under a counter pass
+    (GRBM_GUI_ACTIVE) every set takes the same cycles.  Sets are separated
+    by a fill of a 7-element tensor so that a trace can be split."""
+    torch, bsq = _gpu_setup()
+    import synth
+
+    M = N = K = 4096
+    dev = torch.device("cuda:0")
+    out_path = args.out
+    os.makedirs(os.path.dirname(os.path.abspath(out_path)), exist_ok=True)
+    open(out_path, "w").close()
+    a32, b32 = synth.fp8_blockwise_raw(M, N, K, 204, 205)
+    a32 = torch.from_numpy(a32).to(dev)
+    b32 = torch.from_numpy(b32).to(dev)
+    rq = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    wq = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    sb = torch.empty(N // 128, K // 128, dtype=torch.float32, device=dev)
+    bsq.bsq_quant_fp8_rowblock(a32, rq, sa, 128)
+    bsq.bsq_quant_fp8_tile(b32, wq, sb, 128, 128)
+    del a32, b32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    aq = torch.empty_like(rq)
+    bq = torch.empty_like(wq)
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    marker = torch.empty(7, device=dev)
+    flops = 2.0 * M * N * K
+    for name in OPERAND_SETS:
+        if name == "recipe":
+            aq.copy_(rq)
+            bq.copy_(wq)
+        elif name == "zero":
+            aq.zero_()
+            bq.zero_()
+        elif name == "constant":
+            aq.fill_(0x38)  # e4m3 1.0
+            bq.fill_(0x38)
+        else:
+            # e4m3 codes 0x00..0x7D and their negatives (no NaN)
+            for t in (aq, bq):
+                c = torch.randint(0, 126, t.shape, dtype=torch.uint8, device=dev, generator=gen)
+                c |= (torch.randint(0, 2, t.shape, dtype=torch.uint8, device=dev, generator=gen) << 7)
+                if name == "sparse":
+                    c *= (torch.rand(t.shape, device=dev, generator=gen) < 0.125).to(torch.uint8)
+                t.copy_(c)
+        marker.fill_(0.0)
+        for _ in range(args.warmup):
+            bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y)
+        per = []
+        for _ in range(5):
+            torch.cuda.synchronize()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(args.steps):
+                bsq.bsq_blockwise_fp8_matmul(aq, bq, sa, sb, y)
+            e.record()
+            torch.cuda.synchronize()
+            per.append(s.elapsed_time(e) / args.steps)
+        per.sort()
+        ms = per[2]
+        row = {"operands": name, "m": M, "n": N, "k": K, "launches": args.warmup + 5 * args.steps,
+               "us": round(ms * 1e3, 2), "us_min": round(per[0] * 1e3, 2),
+               "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1)}
+        _log("[operands] " + json.dumps(row))
+        with open(out_path, "a") as f:
+            f.write(json.dumps(row) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -676,6 +765,8 @@ def main():
     ap.add_argument("--suite", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="every row of the block_scaled_mm page's shape table (fp32 and bf16 output)")
+    ap.add_argument("--operand-sweep", action="store_true",
+                    help="the 4096^3 GEMM on operands of different value patterns (clock versus data)")
     ap.add_argument("--out", default=DEFAULT_SUITE_OUT)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -687,6 +778,10 @@ def main():
         sys.exit(2)
     if args.suite:
         run_suite(args)
+    elif args.operand_sweep:
+        if args.out == DEFAULT_SUITE_OUT:
+            args.out = os.path.join(ROOT, "bench_out", "operands.jsonl")
+        run_operand_sweep(args)
     elif args.sweep:
         if args.out == DEFAULT_SUITE_OUT:
             args.out = os.path.join(ROOT, "bench_out", "sweep.jsonl")
