@@ -64,9 +64,36 @@ def _log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _code_text(src: str) -> str:
+    """C++ source without its comments, whitespace runs collapsed to one
+    space: what the compiler reads, so that editing a comment does not
+    change it.  String and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == "/" and src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif c == "/" and src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def _code_hash(path):
+    """sha256 (first 16 hex digits) of a source file's code without comments."""
+    with open(path, encoding="utf-8") as f:
+        return hashlib.sha256(_code_text(f.read()).encode()).hexdigest()[:16]
 
 
 def _gpu_setup():
@@ -248,7 +275,7 @@ def run_main(args):
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("gemm_src_sha256_16") == _src_hash(GEMM_SRC):
+        if tr.get("gemm_code_sha256_16") == _code_hash(GEMM_SRC):
             traffic = tr.get("bytes_per_launch")
     except (OSError, ValueError):
         traffic = None

@@ -17,11 +17,19 @@
 // Both operands are K-contiguous ("TN").  A workgroup of 8 waves owns a
 // 256 x 256 output tile (192 or 128 rows when that fills the CUs in fewer
 // passes) and walks K in steps of 128 bytes; each step's A and B tiles are
-// double-buffered in LDS with a 16-byte-chunk XOR swizzle so the fragment
-// reads are free of bank conflicts.  Wave (wm, wn) owns a quarter of the
-// rows and columns 128*wn..+128: 4 (3, 2) x 8 blocks of 16 x 16.  Products
-// with few tiles run k_gemm_sk instead (64 x 64 tiles, K split over the
-// workgroup's waves).
+// double-buffered in LDS with a 16-byte-chunk XOR swizzle that spreads the
+// 16 rows of a fragment read over the LDS banks.  Wave (wm, wn) owns a
+// quarter of the rows and columns 128*wn..+128: 4 (3, 2) x 8 blocks of
+// 16 x 16.  Products with few tiles run k_gemm_sk instead (64 x 64 tiles, K
+// split over the workgroup's waves).
+//
+// What sets a K-step's length (measured on gfx950, FP8G at 4096^3): each
+// SIMD issues 64 MFMAs, 264 VALU instructions (the rescale) and 48
+// fragment reads per step.  Two waves per SIMD issue an MFMA every 24
+// cycles; each fragment read adds about 14 cycles beside them and each
+// four rescale FMAs about 4, so a step costs about 2460 cycles of the
+// SIMD's issue before its loads and barrier (about 2850 measured).  The
+// tile loads arrive within the step.
 //
 // Unscaled products (FP8G, and the I8/BF16 modes' own instructions): the
 // FP8G calls go through the scaled builtin with all four scale operands
