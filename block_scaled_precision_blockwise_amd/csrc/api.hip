@@ -367,10 +367,24 @@ bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, c
             "workspace too small");
   BSQ_CHECK(D_in <= kMaxInt8Contraction, BSQ_ERR_UNSUPPORTED,
             "D_in > 133144: int32 sums of int8 products could wrap");
-  if (D_in > 0 && D_out > 0) BSQ_CHECK_PTR(workspace);
+  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30), BSQ_ERR_UNSUPPORTED,
+            "extent too large");
+  // every step's pointer rules, checked before anything is enqueued
+  if (B > 0) BSQ_CHECK_PTR(x_s);
+  if (B > 0 && D_in > 0) {
+    BSQ_CHECK_PTR(x);
+    BSQ_CHECK_PTR(x_q);
+  }
+  if (D_out > 0) BSQ_CHECK_PTR(w_s);
+  if (D_in > 0 && D_out > 0) {
+    BSQ_CHECK_PTR(w);
+    BSQ_CHECK_PTR(w_q);
+    BSQ_CHECK_PTR(workspace);
+  }
+  if (B > 0 && D_out > 0) BSQ_CHECK_PTR(y);
+  int8_t* wqT = static_cast<int8_t*>(workspace);
   bsq_status s = bsq_int8_quant_rows(B, D_in, x, x_q, x_s, stream);
   if (s != BSQ_OK) return s;
-  int8_t* wqT = static_cast<int8_t*>(workspace);
   s = bsq_int8_quant_cols(D_in, D_out, w, w_q, w_s, D_in > 0 ? wqT : nullptr, stream);
   if (s != BSQ_OK) return s;
   return bsq_int8_matmul(B, D_in, D_out, x_q, wqT, x_s, w_s, y, nullptr, stream);

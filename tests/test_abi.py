@@ -130,6 +130,17 @@ def test_int8_validation(L):
     assert need >= 4096 * 4096
     _expect(L.bsq_int8_per_channel_matmul(2, 4096, 4096, A16, A16, A16, A16, A16, A16, A16, A16,
                                           need - 1, None), SHAPE, L)
+    # the composite checks every step's arguments before it enqueues any
+    # step: a NULL or misaligned y fails before the device check
+    need = L.bsq_int8_workspace_bytes(64, 16)
+    _expect(L.bsq_int8_per_channel_matmul(2, 64, 16, A16, A16, A16, A16, A16, A16, None, A16, need, None),
+            NULL, L)
+    _expect(L.bsq_int8_per_channel_matmul(2, 64, 16, A16, A16, A16, A16, A16, A16, A4, A16, need, None),
+            ALIGN, L)
+    _expect(L.bsq_int8_per_channel_matmul(2, 64, 16, A16, A16, A16, A16, A16, A16, A16, A4, need, None),
+            ALIGN, L)
+    _expect(L.bsq_int8_per_channel_matmul(2, 64, 16, A16, A16, A16, A16, A16, A16, A16, A16, need, None),
+            DEVICE, L)
 
 
 def test_backward_validation(L):

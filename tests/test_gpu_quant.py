@@ -261,6 +261,37 @@ def test_int8_quantizers(B, Din, Dout):
     assert_bytes_equal(host(wqT), np.ascontiguousarray(rwq.T), "w codes transposed")
 
 
+@pytest.mark.parametrize("B,Din,Dout", [(2048, 4096, 4096), (5, 64, 16), (33, 1000, 336), (3, 4096, 4112),
+                                        (1, 4, 16), (257, 512, 128)])
+def test_int8_composite_on_the_one_pass_column_path(B, Din, Dout):
+    """The composite on shapes whose w takes the one-pass column path
+    (D_in <= 4096, D_in % 4 == 0, D_out % 16 == 0), with the MFMA GEMM or
+    the scalar one: x and w codes and scales bit for bit, y against the
+    oracle's float32 y on every row (sampled rows at the full workload).
+    Odd B, B = 1, 257 stripes of 16 columns."""
+    torch = _torch()
+    from oracle import matmul as OM
+    say("int8 composite, one-pass columns", B, Din, Dout)
+    x, w = synth.int8_workload(B, Din, Dout, 10, 11, zero_rows=(1, 7, 1000), zero_cols=(0, 3, 2047))
+    wq = empty((Din, Dout), torch.int8)
+    ws = empty((Dout,), torch.float32)
+    xq = empty((B, Din), torch.int8)
+    xs = empty((B,), torch.float32)
+    y = empty((B, Dout), torch.float32)
+    work = empty((bsq.bsq_int8_workspace_bytes(Din, Dout),), torch.uint8)
+    bsq.bsq_int8_per_channel_matmul(to_dev(x), to_dev(w), wq, ws, xq, xs, y, work)
+    rxq, rxs = OQ.int8_rows(x)
+    rwq, rws = OQ.int8_cols(w)
+    assert_bytes_equal(host(xs).view(np.uint32), rxs.view(np.uint32), "x scales")
+    assert_bytes_equal(host(ws).view(np.uint32), rws.view(np.uint32), "w scales")
+    assert_bytes_equal(host(xq), rxq, "x codes")
+    assert_bytes_equal(host(wq), rwq, "w codes")
+    rows = np.arange(B) if B <= 512 else np.unique(np.r_[0, 1, 7, 255, 256, 1000, B - 1,
+                                                         np.random.default_rng(5).integers(0, B, 24)])
+    _, _, y32 = OM.int8_matmul(rxq[rows], rwq, rxs[rows], rws)
+    assert_bytes_equal(host(y)[rows].view(np.uint32), y32.view(np.uint32), "y")
+
+
 def test_int8_random_problem_domain():
     """Random cases over the problem's stated domain: B, D_out in 1..6, D_in
     in 1..64, with all-zero rows and columns."""
