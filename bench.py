@@ -451,11 +451,17 @@ def run_suite(args):
               "us_min": round(last["min_ms"] * 1e3, 2), "launches": last["launches"], "bytes": int(nbytes),
               "GB/s": round(gbs, 1), "pct_hbm": round(100 * gbs / PEAK_HBM_GBS, 1)})
 
-    def mfma_row(name, workload, ms, flops, peak):
+    def mfma_row(name, workload, ms, flops, peak, nbytes=None):
         tf = flops / (ms * 1e-3) / 1e12
-        emit({"kernel": name, "workload": workload, "us": round(ms * 1e3, 2),
-              "us_min": round(last["min_ms"] * 1e3, 2), "launches": last["launches"], "flops": flops,
-              "TFLOP/s": round(tf, 1), "pct_peak": round(100 * tf / peak, 1)})
+        row = {"kernel": name, "workload": workload, "us": round(ms * 1e3, 2),
+               "us_min": round(last["min_ms"] * 1e3, 2), "launches": last["launches"], "flops": flops,
+               "TFLOP/s": round(tf, 1), "pct_peak": round(100 * tf / peak, 1)}
+        if nbytes is not None:
+            # roofline of the shape: the MFMA peak or HBM at its arithmetic intensity
+            roof = min(peak, flops / nbytes * PEAK_HBM_GBS / 1e3)
+            row["bound"] = "mfma" if roof >= peak else "hbm"
+            row["pct_roofline"] = round(100 * tf / roof, 1)
+        emit(row)
 
     open(out_path, "w").close()
     # ---- FP8 quantizers (rotating 8 input sets of 64 MB so the 256 MB cache cannot serve them)
@@ -486,8 +492,26 @@ def run_suite(args):
         y = torch.empty(M, N, dtype=torch.float32, device=dev)
         n_it = 20 if M * N * K < 2 ** 38 else 5
         ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(a, b, sa, sb, y), n_it)
-        mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} g128 f32 out", ms, 2 * M * N * K, PEAK_FP8_TFLOPS)
+        mfma_row("gemm_fp8_blockwise", f"{M}x{N}x{K} g128 f32 out", ms, 2 * M * N * K, PEAK_FP8_TFLOPS,
+                 M * K + N * K + (M + N // 128) * (K // 128) * 4 + M * N * 4)
         del a, b, sa, sb, y
+    # ---- the other sweep shapes cold: as many operand sets as exceed
+    # 540 MB (more than twice the 256 MB cache), rotated, so no launch finds
+    # its operands cached
+    for (M, N, K) in synth.FP8_SWEEP:
+        if (M, N, K) == (4096, 4096, 4096):
+            continue  # its own cold row follows
+        per_set = M * K + N * K + (M + N // 128) * (K // 128) * 4
+        n_sets = min(128, -(-540_000_000 // per_set))
+        ops = [(torch.randint(0, 126, (M, K), dtype=torch.uint8, device=dev),
+                torch.randint(0, 126, (N, K), dtype=torch.uint8, device=dev),
+                torch.rand(M, K // 128, device=dev), torch.rand(N // 128, K // 128, device=dev))
+               for _ in range(n_sets)]
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        ms = time_launches(lambda i: bsq.bsq_blockwise_fp8_matmul(*ops[i], y), n_sets, n_sets)
+        mfma_row("gemm_fp8_blockwise (cold operands)", f"{M}x{N}x{K} g128 f32 out, {n_sets} rotating operand sets",
+                 ms, 2 * M * N * K, PEAK_FP8_TFLOPS, per_set + M * N * 4)
+        del ops, y
     # ---- the same GEMM cold: 16 operand sets (512 MiB of codes) rotated, so
     # the 256 MB cache cannot hold the operands between launches
     M = N = K = 4096
