@@ -549,29 +549,31 @@ def run_suite(args):
     del a, b, sa, sb, y, wsn
     # ---- INT8 per-channel
     B, Din, Dout = 2048, 4096, 4096
-    x = torch.randn(B, Din, device=dev)
-    w = 0.02 * torch.randn(Din, Dout, device=dev)
+    # input sets rotated through more than 512 MB, as for the fp8 quantizers
+    xsets = [torch.randn(B, Din, device=dev) for _ in range(16)]
+    wsets = [0.02 * torch.randn(Din, Dout, device=dev) for _ in range(8)]
     xq = torch.empty(B, Din, dtype=torch.int8, device=dev)
     xsc = torch.empty(B, device=dev)
     wq = torch.empty(Din, Dout, dtype=torch.int8, device=dev)
     wsc = torch.empty(Dout, device=dev)
     wqT = torch.empty(Dout, Din, dtype=torch.int8, device=dev)
     yi = torch.empty(B, Dout, device=dev)
-    ms = time_launches(lambda i: bsq.bsq_int8_quant_rows(x, xq, xsc), 40)
+    ms = time_launches(lambda i: bsq.bsq_int8_quant_rows(xsets[i], xq, xsc), 48, 16)
     hbm_row("int8_quant_rows", f"{B}x{Din} f32", ms, B * Din * 5 + B * 4)
-    ms = time_launches(lambda i: bsq.bsq_int8_quant_cols(w, wq, wsc, None), 40)
+    ms = time_launches(lambda i: bsq.bsq_int8_quant_cols(wsets[i], wq, wsc, None), 40, 8)
     hbm_row("int8_quant_cols", f"{Din}x{Dout} f32 (w_q only)", ms, Din * Dout * 5 + Dout * 4)
-    ms = time_launches(lambda i: bsq.bsq_int8_quant_cols(w, wq, wsc, wqT), 40)
+    ms = time_launches(lambda i: bsq.bsq_int8_quant_cols(wsets[i], wq, wsc, wqT), 40, 8)
     hbm_row("int8_quant_cols+T", f"{Din}x{Dout} f32 (w_q and w_qT)", ms, Din * Dout * 6 + Dout * 4)
     ms = time_launches(lambda i: bsq.bsq_int8_matmul(xq, wqT, xsc, wsc, yi), 20)
     mfma_row("gemm_int8", f"{B}x{Dout}x{Din} i32 acc, f32 epilogue", ms, 2 * B * Din * Dout, PEAK_INT8_TOPS)
     # the whole problem: both quantizers and the GEMM
     wk = torch.empty(max(bsq.bsq_int8_workspace_bytes(Din, Dout), 16), dtype=torch.uint8, device=dev)
-    ms = time_launches(lambda i: bsq.bsq_int8_per_channel_matmul(x, w, wq, wsc, xq, xsc, yi, wk), 20)
+    ms = time_launches(lambda i: bsq.bsq_int8_per_channel_matmul(xsets[i], wsets[i % 8], wq, wsc, xq, xsc, yi, wk),
+                       32, 16)
     mfma_row("int8_per_channel (quantize x and w, GEMM)", f"{B}x{Dout}x{Din}", ms, 2 * B * Din * Dout,
              PEAK_INT8_TOPS)
     del wk
-    del x, w, xq, wq, wqT, yi
+    del xsets, wsets, xq, wq, wqT, yi
     # ---- MXFP8 batched scaled_matmul
     Bt, M, N, K = 8, 2048, 2048, 4096
     lhs32 = torch.randn(Bt * M, K, device=dev)
@@ -637,13 +639,15 @@ def run_suite(args):
     del ops
     codes = torch.empty(N, M, dtype=torch.uint8, device=dev)
     scs = torch.empty(N, M // 32, dtype=torch.uint8, device=dev)
-    ms = time_launches(lambda i: bsq.bsq_quant_mx(dY, codes, scs, axis=0, code_dtype=bsq.BSQ_E5M2), 20)
+    # 8 rotating dY of 67 MB: more than 512 MB, so the cache cannot serve them
+    dys = [dY] + [torch.randn(M, N, device=dev).to(torch.bfloat16) for _ in range(7)]
+    ms = time_launches(lambda i: bsq.bsq_quant_mx(dys[i], codes, scs, axis=0, code_dtype=bsq.BSQ_E5M2), 24, 8)
     hbm_row("quant_mx cols^T e5m2", f"{M}x{N} bf16", ms, M * N * 3 + M * N // 32)
     # dY in both orientations (the backward's dX and dW operands) in one pass
     codes_n = torch.empty(M, N, dtype=torch.uint8, device=dev)
     scs_n = torch.empty(M, N // 32, dtype=torch.uint8, device=dev)
-    ms = time_launches(lambda i: bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dY, dyn=(codes_n, scs_n),
-                                                                 dyt=(codes, scs)), 20)
+    ms = time_launches(lambda i: bsq.bsq_mxfp8_backward_quantize(M, N, K, dY=dys[i], dyn=(codes_n, scs_n),
+                                                                 dyt=(codes, scs)), 24, 8)
     hbm_row("quant_mx dY rows + cols^T, one pass, e5m2", f"{M}x{N} bf16", ms, M * N * 4 + M * N // 16)
     _log(f"[suite] wrote {len(rows)} rows to {out_path}")
 
