@@ -204,8 +204,10 @@ bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t*
  * columns, multiply in int8 with int32 sums, apply the float32 epilogue.
  * Writes the five results the problem returns (w_q, w_scales, x_q,
  * x_scales, y).  `workspace` holds the transposed weight codes: at least
- * bsq_int8_workspace_bytes(D_in, D_out) bytes, 16-byte aligned.  Rules as
- * bsq_int8_matmul (D_in <= 133144), checked before anything is enqueued. */
+ * bsq_int8_workspace_bytes(D_in, D_out) bytes, 16-byte aligned.  Rules:
+ * those of bsq_int8_quant_rows, bsq_int8_quant_cols and bsq_int8_matmul
+ * (D_in <= 133144), all checked before any of the three steps is
+ * enqueued. */
 size_t bsq_int8_workspace_bytes(int64_t D_in, int64_t D_out);
 bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, const float* x,
                                        const float* w, int8_t* w_q, float* w_s, int8_t* x_q,
