@@ -136,6 +136,9 @@ bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64
   BSQ_CHECK(rows % group_r == 0 && cols % group_c == 0, BSQ_ERR_SHAPE,
             "rows and cols must be multiples of the tile");
   BSQ_CHECK(group_r == 128 && group_c == 128, BSQ_ERR_UNSUPPORTED, "tile must be 128 x 128");
+  // one workgroup per tile along a one-dimensional grid
+  BSQ_CHECK((rows / 128) * (cols / 128) <= int64_t(0x7FFFFFFF), BSQ_ERR_UNSUPPORTED,
+            "more than 2^31 - 1 tiles");
   if (rows == 0 || cols == 0) return ok();
   BSQ_CHECK_PTR(src);
   BSQ_CHECK_PTR(codes);
@@ -180,9 +183,15 @@ bsq_status bsq_int8_quant_rows(int64_t B, int64_t D, const float* x, int8_t* x_q
   return launch_int8_rows(B, D, x, x_q, x_s, as_stream(stream));
 }
 
+// Longest column the int8 column quantizer takes: its two-pass grids hold
+// D_in / 64 row blocks along y.
+constexpr int64_t kMaxInt8ColsRows = int64_t(64) * 65536;
+
 bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* w_q,
                                float* w_s, int8_t* w_qT, void* stream) {
   BSQ_CHECK(D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(D_in <= kMaxInt8ColsRows, BSQ_ERR_UNSUPPORTED,
+            "D_in > 4194304: beyond the column quantizer's grid");
   if (D_out == 0) return ok();
   BSQ_CHECK_PTR(w_s);
   if (D_in > 0) {
@@ -199,6 +208,14 @@ bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8
 // Longest contraction the GEMM kernels address: their per-lane buffer
 // offsets reach 64 rows of K bytes in 32 bits.
 constexpr int64_t kMaxContraction = int64_t(1) << 24;
+// Longest batch of products: the GEMM grids put the batch along z.
+constexpr int64_t kMaxBatch = 65535;
+// The GEMM grids number one product's output tiles (down to 128 x 256) along
+// x, which holds at most 2^31 - 1.  Composites check this before their first
+// step; a lone product's launcher checks it too.
+static inline bool gemm_tiles_fit(int64_t M, int64_t N) {
+  return ((M + 127) / 128) * ((N + 255) / 256) <= int64_t(0x7FFFFFFF);
+}
 
 bsq_status bsq_blockwise_fp8_matmul(int64_t M, int64_t N, int64_t K, int64_t group_n,
                                     int64_t group_k, const uint8_t* a, const uint8_t* b,
@@ -264,6 +281,7 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
             "the library needs K % 128 == 0 and N % 16 == 0");
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
+  BSQ_CHECK(B <= kMaxBatch, BSQ_ERR_UNSUPPORTED, "batch over 65535");
   GemmLaunch L{};
   const int64_t blk_a = K / K_a, blk_b = K / K_b;  // elements per scale along K
   if (scale_dtype == BSQ_E8M0) {
@@ -499,6 +517,8 @@ bsq_status bwd_check_dims(int64_t M, int64_t N, int64_t K, int code_dtype) {
             "M, N and K must be multiples of 128");
   BSQ_CHECK(M <= kMaxContraction && N <= kMaxContraction && K <= (int64_t(1) << 30),
             BSQ_ERR_UNSUPPORTED, "extent too large");
+  BSQ_CHECK(gemm_tiles_fit(M, K) && gemm_tiles_fit(N, K), BSQ_ERR_UNSUPPORTED,
+            "more than 2^31 - 1 output tiles");
   return BSQ_OK;
 }
 
@@ -709,6 +729,8 @@ bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, c
             "the library needs K % 128 == 0 and N % 16 == 0");
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction / 2,
             BSQ_ERR_UNSUPPORTED, "extent too large");
+  BSQ_CHECK(B <= kMaxBatch, BSQ_ERR_UNSUPPORTED, "batch over 65535");
+  BSQ_CHECK(gemm_tiles_fit(M, N), BSQ_ERR_UNSUPPORTED, "more than 2^31 - 1 output tiles");
   const size_t need = bsq_nvfp4_workspace_bytes(B, M, N, K);
   BSQ_CHECK(workspace_bytes >= need, BSQ_ERR_SHAPE, "workspace too small");
   if (B == 0 || M == 0 || N == 0) return ok();

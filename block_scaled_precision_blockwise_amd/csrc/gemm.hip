@@ -131,17 +131,18 @@ __device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) uint8_t*)(p)));
 }
 
-// Tile order.  Workgroups are dealt to the 8 XCDs round-robin by linear
-// id and each XCD has its own L2, so the tiles one XCD receives should
-// share operand rows: linear id L goes to XCD L % 8 as its (L / 8)-th
-// workgroup; XCD x gets the x-th contiguous eighth of a tile order that
-// walks column-major through bands of kBand tile rows, i.e. a compact
-// block of tiles (4 x 8 for a 16 x 16 grid).
-__device__ __forceinline__ void tile_coords(int& tm, int& tn) {
+// Tile order.  The grid is one-dimensional over the tiles (the batch in
+// z): its x extent allows 2^31 - 1 workgroups where y allows 65536.
+// Workgroups are dealt to the 8 XCDs round-robin by linear id and each XCD
+// has its own L2, so the tiles one XCD receives should share operand rows:
+// linear id L goes to XCD L % 8 as its (L / 8)-th workgroup; XCD x gets the
+// x-th contiguous eighth of a tile order that walks column-major through
+// bands of kBand tile rows, i.e. a compact block of tiles (4 x 8 for a
+// 16 x 16 grid).
+__device__ __forceinline__ void tile_coords(int& tm, int& tn, int tiles_m, int tiles_n) {
   constexpr int kBand = 4;
-  const int tiles_n = gridDim.x, tiles_m = gridDim.y;
   const int T = tiles_n * tiles_m;
-  const int L = blockIdx.y * tiles_n + blockIdx.x;
+  const int L = blockIdx.x;
   const int per = T / 8;
   const int t = (L < 8 * per) ? (L % 8) * per + L / 8 : L;
   const int band = t / (kBand * tiles_n);
@@ -293,7 +294,7 @@ __global__ void __launch_bounds__(64 * NW, 1) k_gemm(GemmArgs p) {
   const int tid = threadIdx.x;
   const int batch = blockIdx.z;
   int tm, tn;
-  tile_coords(tm, tn);
+  tile_coords(tm, tn, (p.M + TBM - 1) / TBM, (p.N + BN - 1) / BN);
   const int m0 = tm * TBM;
   const int n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
@@ -945,9 +946,15 @@ void launch_gemm_kernel(Kernel k, dim3 grid, dim3 block, hipStream_t st, Args...
 template <int MODE, int OUT_BF16, int FA, int FB, int GN1, int GEN = 0, int SUB = 0>
 bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   const int64_t tiles = int64_t((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * batch;
+  // big-tile grids: all tiles of a product along x, the batch along z
+  auto big_grid = [&](int rows) {
+    return dim3(unsigned(((a.M + rows - 1) / rows) * ((a.N + BN - 1) / BN)), 1u, unsigned(batch));
+  };
+  if (int64_t((a.M + 127) / 128) * ((a.N + BN - 1) / BN) > int64_t(0x7FFFFFFF) || batch > 65535)
+    return fail(BSQ_ERR_UNSUPPORTED, "more than 2^31 - 1 tiles, or a batch over 65535");
   if constexpr (GEN != 0) {
     // general scale blocks: the big-tile kernel at every size
-    dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + BM - 1) / BM), unsigned(batch));
+    const dim3 grid = big_grid(BM);
     launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, 8, 256, 1, SUB>, grid, dim3(512), st, a);
     return launch_status("gemm (general scale blocks)");
   }
@@ -964,7 +971,7 @@ bsq_status run(const GemmArgs& a, int batch, hipStream_t st) {
   }
   constexpr int NW = 8;
   const int rows = tile_rows_for(a.M, a.N, batch);
-  dim3 grid(unsigned((a.N + BN - 1) / BN), unsigned((a.M + rows - 1) / rows), unsigned(batch));
+  const dim3 grid = big_grid(rows);
   if (rows == 128)
     launch_gemm_kernel(k_gemm<MODE, OUT_BF16, FA, FB, GN1, NW, 128>, grid, dim3(64 * NW), st, a);
   else if (rows == 192)

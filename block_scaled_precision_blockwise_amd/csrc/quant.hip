@@ -141,8 +141,9 @@ __global__ void __launch_bounds__(256) k_fp8_rowblock(const float4* __restrict__
 }
 
 // ------------------------------------------------ fp8 128 x 128 tiles ----
-// One workgroup per tile; each thread holds 64 values (16 float4) of the
-// tile in registers between the reduction and the encode.
+// One workgroup per tile, tiles numbered row-major along a one-dimensional
+// grid; each thread holds 64 values (16 float4) of the tile in registers
+// between the reduction and the encode.
 __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ src,
                                                      uint8_t* __restrict__ codes,
                                                      float* __restrict__ scales, int64_t cols) {
@@ -150,8 +151,10 @@ __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ s
   const int tx = threadIdx.x;
   const int c4 = tx & 31;
   const int r0 = tx >> 5;
-  const int64_t row0 = int64_t(blockIdx.y) * 128;
-  const int64_t col0 = int64_t(blockIdx.x) * 128 + 4 * c4;
+  const int64_t tiles_c = cols / 128;
+  const int64_t t = blockIdx.x;
+  const int64_t row0 = (t / tiles_c) * 128;
+  const int64_t col0 = (t % tiles_c) * 128 + 4 * c4;
   float4 v[16];
   uint32_t m = 0u;
 #pragma unroll
@@ -171,7 +174,7 @@ __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ s
     uint32_t* q = reinterpret_cast<uint32_t*>(codes + (row0 + r0 + 8 * i) * cols + col0);
     *q = quant4_e4m3(v[i], s, r);
   }
-  if (tx == 0) scales[int64_t(blockIdx.y) * gridDim.x + blockIdx.x] = s;
+  if (tx == 0) scales[t] = s;
 }
 
 // ------------------------------------------------------------ MX (e8m0) --
@@ -606,6 +609,8 @@ __global__ void __launch_bounds__(256) k_int8_col_scales(const uint32_t* __restr
 // each XCD's share of a row is a contiguous 2 KiB (at D_out = 4096), which
 // spans all of its L2 channels (a 512-byte share did not).
 constexpr int kOnePassMaxRows = 4096;
+// the two-pass path's grids hold D_in / 64 row blocks along y (at most 65536)
+constexpr int64_t kTwoPassMaxRows = int64_t(64) * 65536;
 __global__ void __launch_bounds__(512) k_int8_cols_onepass(const float* __restrict__ w,
                                                            int8_t* __restrict__ wq,
                                                            float* __restrict__ ws,
@@ -765,7 +770,7 @@ bsq_status launch_fp8_rowblock(int64_t rows, int64_t cols, int64_t group, const 
 bsq_status launch_fp8_tile128(int64_t rows, int64_t cols, const float* src, uint8_t* codes,
                               float* scales, hipStream_t st) {
   if (rows == 0 || cols == 0) return ok();
-  dim3 grid(unsigned(cols / 128), unsigned(rows / 128));
+  const dim3 grid{unsigned((rows / 128) * (cols / 128))};  // at most 2^31 - 1 tiles (checked by the caller)
   hipLaunchKernelGGL(k_fp8_tile128, grid, 256, 0, st, src, codes, scales, cols);
   return launch_status("quant_fp8_tile");
 }
@@ -856,6 +861,8 @@ bsq_status launch_int8_cols(int64_t D_in, int64_t D_out, const float* w, int8_t*
                        D_in, D_out);
     return launch_status("int8_quant_cols");
   }
+  // the two-pass grids put D_in / 64 and D_in / 128 row blocks along y
+  if (D_in > kTwoPassMaxRows) return fail(BSQ_ERR_UNSUPPORTED, "int8 column quantizer: D_in > 4194304");
   uint32_t* cmax = reinterpret_cast<uint32_t*>(ws);  // column maxima live in w_s until the end
   hipLaunchKernelGGL(k_fill_u32, grid_for(D_out, 256), 256, 0, st, cmax, D_out, 0u);
   if (D_in > 0) {

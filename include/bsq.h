@@ -15,9 +15,11 @@
  *     enqueued and bsq_last_error() (thread-local) describes the cause.
  *   - A call with an empty extent (a zero size) is a valid no-op unless the
  *     call's own rules say otherwise.
- *   - Matmul extents are at most 2^30, and a contraction length (K of a
+ *   - Matmul extents are at most 2^30, a contraction length (K of a
  *     matmul; M and N of the mxfp8 backward, whose two products contract
- *     over them) at most 2^24; larger -> BSQ_ERR_UNSUPPORTED.
+ *     over them) at most 2^24, a batch of products at most 65535, and one
+ *     product's output at most 2^31 - 1 tiles of 128 x 256 (far beyond any
+ *     output that fits in memory); larger -> BSQ_ERR_UNSUPPORTED.
  *   - Non-finite inputs give unspecified results (the pages state all
  *     values are finite).
  *   - Format names: E4M3 = OCP float8_e4m3fn, E5M2 = OCP float8_e5m2,
@@ -106,7 +108,7 @@ bsq_status bsq_quant_fp8_rowblock(int64_t rows, int64_t cols, int64_t group,
  *   codes  uint8   [rows, cols]                        (E4M3, out)
  *   scales float32 [rows / group_r, cols / group_c]    (out)
  * Rules: rows % group_r == 0, cols % group_c == 0; the library runs
- * group_r == group_c == 128. */
+ * group_r == group_c == 128, at most 2^31 - 1 tiles. */
 bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64_t group_c,
                               const float* src, uint8_t* codes, float* scales, void* stream);
 
@@ -141,7 +143,8 @@ bsq_status bsq_int8_quant_rows(int64_t B, int64_t D, const float* x, int8_t* x_q
  *   w_q  [D_in, D_out] int8 (w's layout, out)
  *   w_s  [D_out] float32 (out)
  *   w_qT [D_out, D_in] int8, the same codes transposed (K-contiguous, for
- *        bsq_int8_matmul), or NULL to skip. */
+ *        bsq_int8_matmul), or NULL to skip.
+ * Rules: D_in <= 4194304 (2^22), else UNSUPPORTED. */
 bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8_t* w_q,
                                float* w_s, int8_t* w_qT, void* stream);
 

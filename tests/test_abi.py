@@ -180,6 +180,32 @@ def test_contraction_length_limit(L):
         _expect(f(M, N, 256, A16, A16, A16, E5, BF, A16, A16, A16, 1 << 62, None), UNSUP, L)
 
 
+def test_grid_limits(L):
+    """Launch-grid limits are refused on the host: a batch of products
+    runs along the grid's z (at most 65535), one product's output tiles and
+    the tile quantizer's tiles along x (at most 2^31 - 1), and the int8
+    column quantizer's two-pass row blocks along y (D_in at most 2^22)."""
+    E4, E8, F32 = bsq.BSQ_E4M3, bsq.BSQ_E8M0, bsq.BSQ_F32
+    sm = L.bsq_scaled_matmul
+    _expect(sm(65536, 8, 16, 128, 4, 4, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), UNSUP, L)
+    _expect(sm(65535, 8, 16, 128, 4, 4, A16, E4, A16, E4, A16, A16, E8, A16, F32, None), DEVICE, L)
+    nv = L.bsq_scaled_matmul_nvfp4
+    _expect(nv(65536, 16, 32, 256, A16, A16, A16, A16, A16, F32, A16, 1 << 62, None), UNSUP, L)
+    _expect(nv(65535, 16, 32, 256, A16, A16, A16, A16, A16, F32, A16, 1 << 62, None), DEVICE, L)
+    # 2^23 x 2^22 output tiles of 128 x 256
+    _expect(nv(1, 1 << 30, 1 << 30, 128, A16, A16, A16, A16, A16, F32, A16, 1 << 62, None), UNSUP, L)
+    # the backward's dX product, M x K = 2^24 x 2^30: 2^39 tiles
+    E5, BF = bsq.BSQ_E5M2, bsq.BSQ_BF16
+    _expect(L.bsq_mxfp8_backward(1 << 24, 256, 1 << 30, A16, A16, A16, E5, BF, A16, A16, A16,
+                                 1 << 62, None), UNSUP, L)
+    # the tile quantizer: 2^16 x 2^16 tiles of 128 x 128
+    _expect(L.bsq_quant_fp8_tile(1 << 23, 1 << 23, 128, 128, A16, A16, A16, None), UNSUP, L)
+    _expect(L.bsq_quant_fp8_tile(1 << 20, 1 << 20, 128, 128, A16, A16, A16, None), DEVICE, L)
+    qc = L.bsq_int8_quant_cols
+    _expect(qc((1 << 22) + 1, 16, A16, A16, A16, A16, None), UNSUP, L)
+    _expect(qc(1 << 22, 16, A16, A16, A16, A16, None), DEVICE, L)
+
+
 def test_backward_split_validation(L):
     """The two-call backward: an operand is produced iff its codes pointer
     is given; a product is computed iff its output pointer is given."""

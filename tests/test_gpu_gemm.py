@@ -167,6 +167,34 @@ def test_blockwise_sweep_sampled(M, N, K):
     assert np.all(np.isfinite(y)), "unwritten output"
 
 
+def test_blockwise_more_tile_rows_than_grid_y():
+    """M = 65537 x 256: more tile rows than a grid's y extent holds (65536),
+    launched on the one-dimensional tile grid.  A's codes repeat with a
+    period of 4099 rows (no multiple of a tile height) and its scales are
+    drawn per row, so no tile equals the one 65536 tile rows before it;
+    the sampled rows take both sides of the 65536th tile row and both
+    ends."""
+    torch = _torch()
+    M, N, K, P = 65537 * 256, 256, 128, 4099
+    say("blockwise beyond grid y", M, N, K)
+    a_blk = synth.random_fp8_codes((P, K), 880, "e4m3")
+    b = synth.random_fp8_codes((N, K), 881, "e4m3")
+    sa = synth.random_f32_scales((M, K // 128), 882)
+    sb = synth.random_f32_scales((N // 128, K // 128), 883)
+    a = to_dev(a_blk).repeat(-(-M // P), 1)[:M]
+    y = filled((M, N), torch.float32, float("nan"))
+    bsq.bsq_blockwise_fp8_matmul(a, to_dev(b), to_dev(sa), to_dev(sb), y, group_n=128, group_k=128)
+    edge = 65536 * 256
+    rows = {0, 1, 255, 256, M // 2, edge - 257, edge - 256, edge - 1, edge, edge + 1, edge + 255, M - 1}
+    rows |= set(int(v) for v in np.random.default_rng(884).choice(M, 40, replace=False))
+    rows = np.array(sorted(rows))
+    yh = host(y[torch.from_numpy(rows).to(y.device)])
+    ar = a_blk[rows % P]
+    yr, T = OM.blockwise_fp8(ar, b, sa[rows], sb)
+    assert_within_T_hw(yh, yr, T, _blockwise_hw_bound(ar, b, sa[rows], sb), "y rows")
+    assert not bool(torch.isnan(y).any()), "unwritten output"
+
+
 def test_blockwise_from_quantized_randn_full_size():
     """The headline shape with operands from the recipe (randn quantized by
     the GPU quantizers), checked on sampled rows."""

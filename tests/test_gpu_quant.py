@@ -97,6 +97,27 @@ def test_fp8_tile(shape):
     assert_bytes_equal(host(c), rc, "codes")
 
 
+def test_fp8_tile_more_tile_rows_than_grid_y():
+    """65538 x 2 tiles of 128 x 128, more tile rows than a grid's y extent
+    holds (65536), on the one-dimensional tile grid.  The source repeats
+    with a period of 4099 rows, so no tile equals the one 65536 tile rows
+    before it; tile rows at both ends and on both sides of the 65536th are
+    compared with the oracle byte for byte."""
+    torch = _torch()
+    R, C, P = 65538 * 128, 256, 4099
+    say("fp8_tile beyond grid y", R, C)
+    blk = synth.randn_f32((P, C), 890)
+    src = to_dev(blk).repeat(-(-R // P), 1)[:R]
+    c = empty((R, C), torch.uint8)
+    s = empty((R // 128, C // 128), torch.float32)
+    bsq.bsq_quant_fp8_tile(src, c, s, 128, 128)
+    for t in (0, 32768, 65535, 65536, 65537):
+        rows = np.arange(t * 128, (t + 1) * 128)
+        rc, rs = OQ.fp8_tile(blk[rows % P], 128, 128)
+        assert_bytes_equal(host(s[t:t + 1]).view(np.uint32), rs.view(np.uint32), f"scales tile row {t}")
+        assert_bytes_equal(host(c[t * 128:(t + 1) * 128]), rc, f"codes tile row {t}")
+
+
 def _mx_input(shape, seed, bf16):
     x = synth.randn_f32(shape, seed)
     if shape[0] >= 3 and shape[1] >= 64:
@@ -257,6 +278,27 @@ def test_int8_quantizers(B, Din, Dout):
     assert_bytes_equal(host(xs).view(np.uint32), rxs.view(np.uint32), "x scales")
     assert_bytes_equal(host(ws).view(np.uint32), rws.view(np.uint32), "w scales")
     assert_bytes_equal(host(xq), rxq, "x codes")
+    assert_bytes_equal(host(wq), rwq, "w codes")
+    assert_bytes_equal(host(wqT), np.ascontiguousarray(rwq.T), "w codes transposed")
+
+
+def test_int8_cols_longest_column():
+    """D_in = 2^22, the longest column the column quantizer takes: its
+    two-pass grids then hold 65536 row blocks of 64 along y, the most a
+    grid allows.  Column maxima placed in the first and last row blocks."""
+    torch = _torch()
+    Din, Dout = 1 << 22, 16
+    say("int8 cols longest", Din, Dout)
+    w = synth.randn_f32((Din, Dout), 895, std=0.02)
+    w[Din - 3, 5] = 0.5
+    w[2, 9] = -0.5
+    w[:, 12] = 0.0
+    wq = empty((Din, Dout), torch.int8)
+    ws = empty((Dout,), torch.float32)
+    wqT = empty((Dout, Din), torch.int8)
+    bsq.bsq_int8_quant_cols(to_dev(w), wq, ws, wqT)
+    rwq, rws = OQ.int8_cols(w)
+    assert_bytes_equal(host(ws).view(np.uint32), rws.view(np.uint32), "w scales")
     assert_bytes_equal(host(wq), rwq, "w codes")
     assert_bytes_equal(host(wqT), np.ascontiguousarray(rwq.T), "w codes transposed")
 
