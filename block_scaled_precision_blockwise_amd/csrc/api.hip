@@ -1,5 +1,6 @@
 // The C ABI of libbsq (declared in include/bsq.h): argument validation on
 // the host, then kernel launches on the caller's stream.
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -373,7 +374,9 @@ bsq_status bsq_int8_matmul(int64_t B, int64_t D_in, int64_t D_out, const int8_t*
 
 size_t bsq_int8_workspace_bytes(int64_t D_in, int64_t D_out) {
   if (D_in <= 0 || D_out <= 0) return 0;
-  return size_t((D_in * D_out + 255) / 256 * 256);
+  int64_t n = 0;
+  if (__builtin_mul_overflow(D_in, D_out, &n) || n > (int64_t(1) << 62)) return SIZE_MAX;
+  return size_t((n + 255) / 256 * 256);
 }
 
 bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, const float* x,
@@ -381,12 +384,12 @@ bsq_status bsq_int8_per_channel_matmul(int64_t B, int64_t D_in, int64_t D_out, c
                                        float* x_s, float* y, void* workspace,
                                        size_t workspace_bytes, void* stream) {
   BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
-  BSQ_CHECK(workspace_bytes >= bsq_int8_workspace_bytes(D_in, D_out), BSQ_ERR_SHAPE,
-            "workspace too small");
   BSQ_CHECK(D_in <= kMaxInt8Contraction, BSQ_ERR_UNSUPPORTED,
             "D_in > 133144: int32 sums of int8 products could wrap");
   BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30), BSQ_ERR_UNSUPPORTED,
             "extent too large");
+  BSQ_CHECK(workspace_bytes >= bsq_int8_workspace_bytes(D_in, D_out), BSQ_ERR_SHAPE,
+            "workspace too small");
   // every step's pointer rules, checked before anything is enqueued
   if (B > 0) BSQ_CHECK_PTR(x_s);
   if (B > 0 && D_in > 0) {
@@ -461,6 +464,8 @@ bsq_status bsq_int8_per_channel_matmul_noalloc(int64_t B, int64_t D_in, int64_t 
   BSQ_CHECK(B >= 0 && D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
   BSQ_CHECK(D_in <= kMaxInt8Contraction, BSQ_ERR_UNSUPPORTED,
             "D_in > 133144: int32 sums of int8 products could wrap");
+  BSQ_CHECK(B <= (int64_t(1) << 30) && D_out <= (int64_t(1) << 30), BSQ_ERR_UNSUPPORTED,
+            "extent too large");
   const size_t need = bsq_int8_workspace_bytes(D_in, D_out);
   BSQ_CHECK(need <= kNoAllocScratchBytes, BSQ_ERR_UNSUPPORTED,
             "D_in * D_out exceeds the 16 MiB scratch of the no-allocation entry point");
@@ -592,6 +597,9 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K) {
 
 size_t bsq_mxfp8_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return 0;
+  // beyond the call's extents the byte count could overflow; no buffer is
+  // large enough for such sizes
+  if (M > kMaxContraction || N > kMaxContraction || K > (int64_t(1) << 30)) return SIZE_MAX;
   return bwd_layout(M, N, K).total;
 }
 
@@ -711,8 +719,18 @@ bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dt
 
 // ------------------------------------------------------------- nvfp4 --
 
+// Largest operand of the nvfp4 product, in values (B * M * K and B * N * K):
+// its bfloat16 copy then takes at most 2 TiB, far beyond device memory,
+// and every size derived from it fits 64 bits.
+constexpr int64_t kMaxNvfp4Values = int64_t(1) << 40;
+static inline bool nvfp4_operand_fits(int64_t B, int64_t R, int64_t K) {
+  int64_t n = 0;
+  return !__builtin_mul_overflow(B, R, &n) && !__builtin_mul_overflow(n, K, &n) && n <= kMaxNvfp4Values;
+}
+
 size_t bsq_nvfp4_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K) {
   if (B < 0 || M < 0 || N < 0 || K < 0) return 0;
+  if (!nvfp4_operand_fits(B, M, K) || !nvfp4_operand_fits(B, N, K)) return SIZE_MAX;
   return up256(size_t(B * M * K * 2)) + up256(size_t(B * N * K * 2));
 }
 
@@ -731,6 +749,8 @@ bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, c
             BSQ_ERR_UNSUPPORTED, "extent too large");
   BSQ_CHECK(B <= kMaxBatch, BSQ_ERR_UNSUPPORTED, "batch over 65535");
   BSQ_CHECK(gemm_tiles_fit(M, N), BSQ_ERR_UNSUPPORTED, "more than 2^31 - 1 output tiles");
+  BSQ_CHECK(nvfp4_operand_fits(B, M, K) && nvfp4_operand_fits(B, N, K), BSQ_ERR_UNSUPPORTED,
+            "an operand of more than 2^40 values");
   const size_t need = bsq_nvfp4_workspace_bytes(B, M, N, K);
   BSQ_CHECK(workspace_bytes >= need, BSQ_ERR_SHAPE, "workspace too small");
   if (B == 0 || M == 0 || N == 0) return ok();

@@ -20,6 +20,8 @@
  *     over them) at most 2^24, a batch of products at most 65535, and one
  *     product's output at most 2^31 - 1 tiles of 128 x 256 (far beyond any
  *     output that fits in memory); larger -> BSQ_ERR_UNSUPPORTED.
+ *   - A *_workspace_bytes query returns 0 for negative sizes and SIZE_MAX
+ *     for sizes whose byte count would not fit (its call rejects them).
  *   - Non-finite inputs give unspecified results (the pages state all
  *     values are finite).
  *   - Format names: E4M3 = OCP float8_e4m3fn, E5M2 = OCP float8_e5m2,
@@ -306,8 +308,9 @@ bsq_status bsq_mxfp8_backward_gemms(int64_t M, int64_t N, int64_t K, int code_dt
  *       receives both operands dequantized to bfloat16 (exact: an e2m1
  *       value times an e4m3 scale has at most 6 significant bits), which
  *       a bf16 matrix-core product then multiplies in float32.
- * Rules: K % 16 == 0 (else SHAPE); the library needs K % 128 == 0 and
- * N % 16 == 0 (else UNSUPPORTED); a smaller workspace -> SHAPE. */
+ * Rules: K % 16 == 0 (else SHAPE); the library needs K % 128 == 0,
+ * N % 16 == 0 and B * M * K, B * N * K <= 2^40 (else UNSUPPORTED); a
+ * smaller workspace -> SHAPE. */
 size_t bsq_nvfp4_workspace_bytes(int64_t B, int64_t M, int64_t N, int64_t K);
 bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, const uint8_t* lhs,
                                    const uint8_t* rhs, const uint8_t* lhs_scales,

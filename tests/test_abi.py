@@ -206,6 +206,30 @@ def test_grid_limits(L):
     _expect(qc(1 << 22, 16, A16, A16, A16, A16, None), DEVICE, L)
 
 
+def test_workspace_queries_never_wrap(L):
+    """A size query whose byte count would not fit 64 bits returns SIZE_MAX
+    (no buffer suffices) instead of a wrapped small number, and its call
+    rejects such sizes as UNSUPPORTED before comparing workspaces."""
+    SIZE_MAX = 2 ** 64 - 1
+    assert L.bsq_int8_workspace_bytes(1 << 40, 1 << 40) == SIZE_MAX
+    assert L.bsq_int8_workspace_bytes(133144, 1 << 30) == 133144 * (1 << 30)
+    assert L.bsq_mxfp8_backward_workspace_bytes(1 << 40, 1 << 40, 1 << 40) == SIZE_MAX
+    assert L.bsq_nvfp4_workspace_bytes(65535, 1 << 30, 16, 1 << 23) == SIZE_MAX
+    assert L.bsq_nvfp4_workspace_bytes(1, 1 << 20, 16, 1 << 20) == 2 * (1 << 40) + 2 * (1 << 24)
+    assert L.bsq_int8_workspace_bytes(-1, 5) == 0
+    F32 = bsq.BSQ_F32
+    # nvfp4: B*M*K = 2^16 * 2^30 * 2^23 would wrap int64; refused, whatever workspace is claimed
+    _expect(L.bsq_scaled_matmul_nvfp4(65535, 1 << 30, 16, 1 << 23, A16, A16, A16, A16, A16, F32, A16,
+                                      SIZE_MAX, None), UNSUP, L)
+    _expect(L.bsq_scaled_matmul_nvfp4(1, (1 << 40) // 128 + 1, 16, 128, A16, A16, A16, A16, A16, F32,
+                                      A16, SIZE_MAX, None), UNSUP, L)
+    # int8 composite and its no-allocation form: extents before the workspace
+    _expect(L.bsq_int8_per_channel_matmul(4, 128, 1 << 40, A16, A16, A16, A16, A16, A16, A16, A16, 0,
+                                          None), UNSUP, L)
+    _expect(L.bsq_int8_per_channel_matmul_noalloc(4, 128, 1 << 62, A16, A16, A16, A16, A16, A16, A16,
+                                                  None), UNSUP, L)
+
+
 def test_backward_split_validation(L):
     """The two-call backward: an operand is produced iff its codes pointer
     is given; a product is computed iff its output pointer is given."""
