@@ -286,6 +286,8 @@ def bsq_blockwise_fp8_matmul(a, b, a_scales, b_scales, out, group_n: int = 128, 
     """block_scaled_mm: a [M, K], b [N, K] E4M3 codes; a_scales f32 [M, K/gk];
     b_scales f32 [N/gn, K/gk]; out f32 or bf16 [M, N]."""
     torch = _torch()
+    if group_n <= 0 or group_k <= 0:
+        raise ValueError("group_n and group_k must be positive")
     _dev(a, b, a_scales, b_scales, out)
     M, K = a.shape
     N = b.shape[0]
