@@ -26,10 +26,13 @@
 // What sets a K-step's length (measured on gfx950, FP8G at 4096^3): each
 // SIMD issues 64 MFMAs, 264 VALU instructions (the rescale) and 48
 // fragment reads per step.  Two waves per SIMD issue an MFMA every 24
-// cycles; each fragment read adds about 14 cycles beside them and each
-// four rescale FMAs about 4, so a step costs about 2460 cycles of the
-// SIMD's issue before its loads and barrier (about 2850 measured).  The
-// tile loads arrive within the step.
+// cycles alone; with the step's reads and rescale FMAs beside them, about
+// every 36 (reads or FMAs alone cost little; together they do), so the
+// step's register-side work takes about 2310 cycles of the SIMD's issue
+// before its loads and barrier (about 2850 measured).  The tile loads
+// arrive within the step.  The 32x32x64 MFMA, with each block's two K
+// halves chained for the rescale, took more cycles per step than this
+// layout.
 //
 // Unscaled products (FP8G, and the I8/BF16 modes' own instructions): the
 // FP8G calls go through the scaled builtin with all four scale operands
