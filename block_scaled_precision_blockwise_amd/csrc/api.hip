@@ -114,11 +114,21 @@ bsq_status bsq_time_next_gemm(void* start_event, void* stop_event) {
   return ok();
 }
 
+// Largest array the calls take, in elements: far beyond device memory, and
+// small enough that every byte offset derived from it fits 64 bits.
+constexpr int64_t kMaxElems = int64_t(1) << 60;
+// a * b * c <= kMaxElems for non-negative factors, without overflow
+static inline bool elems_fit(int64_t a, int64_t b, int64_t c = 1) {
+  int64_t n = 0;
+  return !__builtin_mul_overflow(a, b, &n) && !__builtin_mul_overflow(n, c, &n) && n <= kMaxElems;
+}
+
 // ------------------------------------------------------------ quantizers --
 
 bsq_status bsq_quant_fp8_rowblock(int64_t rows, int64_t cols, int64_t group, const float* src,
                                   uint8_t* codes, float* scales, void* stream) {
   BSQ_CHECK(rows >= 0 && cols >= 0 && group > 0, BSQ_ERR_SHAPE, "negative size or group <= 0");
+  BSQ_CHECK(elems_fit(rows, cols), BSQ_ERR_UNSUPPORTED, "more than 2^60 elements");
   BSQ_CHECK(cols % group == 0, BSQ_ERR_SHAPE, "cols must be a multiple of group");
   BSQ_CHECK(group == 32 || group == 64 || group == 128 || group == 256, BSQ_ERR_UNSUPPORTED,
             "group must be 32, 64, 128 or 256");
@@ -134,6 +144,7 @@ bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64
                               const float* src, uint8_t* codes, float* scales, void* stream) {
   BSQ_CHECK(rows >= 0 && cols >= 0 && group_r > 0 && group_c > 0, BSQ_ERR_SHAPE,
             "negative size or group <= 0");
+  BSQ_CHECK(elems_fit(rows, cols), BSQ_ERR_UNSUPPORTED, "more than 2^60 elements");
   BSQ_CHECK(rows % group_r == 0 && cols % group_c == 0, BSQ_ERR_SHAPE,
             "rows and cols must be multiples of the tile");
   BSQ_CHECK(group_r == 128 && group_c == 128, BSQ_ERR_UNSUPPORTED, "tile must be 128 x 128");
@@ -151,6 +162,7 @@ bsq_status bsq_quant_fp8_tile(int64_t rows, int64_t cols, int64_t group_r, int64
 bsq_status bsq_quant_mx(int64_t rows, int64_t cols, int axis, const void* src, int src_dtype,
                         uint8_t* codes, int code_dtype, uint8_t* scales, void* stream) {
   BSQ_CHECK(rows >= 0 && cols >= 0, BSQ_ERR_SHAPE, "negative size");
+  BSQ_CHECK(elems_fit(rows, cols), BSQ_ERR_UNSUPPORTED, "more than 2^60 elements");
   BSQ_CHECK(axis == 0 || axis == 1, BSQ_ERR_SHAPE, "axis must be 0 or 1");
   BSQ_CHECK(known_dtype(src_dtype) && known_dtype(code_dtype), BSQ_ERR_DTYPE, "unknown dtype");
   BSQ_CHECK(src_dtype == BSQ_F32 || src_dtype == BSQ_BF16, BSQ_ERR_UNSUPPORTED,
@@ -174,6 +186,9 @@ bsq_status bsq_quant_mx(int64_t rows, int64_t cols, int axis, const void* src, i
 bsq_status bsq_int8_quant_rows(int64_t B, int64_t D, const float* x, int8_t* x_q, float* x_s,
                                void* stream) {
   BSQ_CHECK(B >= 0 && D >= 0, BSQ_ERR_SHAPE, "negative size");
+  // one workgroup per row along the grid's x
+  BSQ_CHECK(B <= int64_t(0x7FFFFFFF), BSQ_ERR_UNSUPPORTED, "B > 2^31 - 1 rows");
+  BSQ_CHECK(elems_fit(B, D), BSQ_ERR_UNSUPPORTED, "more than 2^60 elements");
   if (B == 0) return ok();
   BSQ_CHECK_PTR(x_s);
   if (D > 0) {
@@ -193,6 +208,7 @@ bsq_status bsq_int8_quant_cols(int64_t D_in, int64_t D_out, const float* w, int8
   BSQ_CHECK(D_in >= 0 && D_out >= 0, BSQ_ERR_SHAPE, "negative size");
   BSQ_CHECK(D_in <= kMaxInt8ColsRows, BSQ_ERR_UNSUPPORTED,
             "D_in > 4194304: beyond the column quantizer's grid");
+  BSQ_CHECK(elems_fit(D_in, D_out), BSQ_ERR_UNSUPPORTED, "more than 2^60 elements");
   if (D_out == 0) return ok();
   BSQ_CHECK_PTR(w_s);
   if (D_in > 0) {
@@ -283,6 +299,8 @@ bsq_status bsq_scaled_matmul(int64_t B, int64_t M, int64_t N, int64_t K, int64_t
   BSQ_CHECK(M <= (int64_t(1) << 30) && N <= (int64_t(1) << 30) && K <= kMaxContraction,
             BSQ_ERR_UNSUPPORTED, "extent too large");
   BSQ_CHECK(B <= kMaxBatch, BSQ_ERR_UNSUPPORTED, "batch over 65535");
+  BSQ_CHECK(elems_fit(B, M, K) && elems_fit(B, N, K) && elems_fit(B, M, N), BSQ_ERR_UNSUPPORTED,
+            "an operand or the output of more than 2^60 elements");
   GemmLaunch L{};
   const int64_t blk_a = K / K_a, blk_b = K / K_b;  // elements per scale along K
   if (scale_dtype == BSQ_E8M0) {
@@ -751,6 +769,7 @@ bsq_status bsq_scaled_matmul_nvfp4(int64_t B, int64_t M, int64_t N, int64_t K, c
   BSQ_CHECK(gemm_tiles_fit(M, N), BSQ_ERR_UNSUPPORTED, "more than 2^31 - 1 output tiles");
   BSQ_CHECK(nvfp4_operand_fits(B, M, K) && nvfp4_operand_fits(B, N, K), BSQ_ERR_UNSUPPORTED,
             "an operand of more than 2^40 values");
+  BSQ_CHECK(elems_fit(B, M, N), BSQ_ERR_UNSUPPORTED, "an output of more than 2^60 elements");
   const size_t need = bsq_nvfp4_workspace_bytes(B, M, N, K);
   BSQ_CHECK(workspace_bytes >= need, BSQ_ERR_SHAPE, "workspace too small");
   if (B == 0 || M == 0 || N == 0) return ok();

@@ -811,10 +811,13 @@ bsq_status launch_mx_cols(const MxT* jobs, int n, bool src_bf16, bool e5m2, hipS
     j.row_scales = jobs[i].row_scales;
     j.rows = jobs[i].rows;
     j.cols = jobs[i].cols;
-    j.tiles_x = int((jobs[i].cols + 63) / 64);
-    j.first = blocks;
-    const int64_t tiles = int64_t(j.tiles_x) * ((jobs[i].rows + 63) / 64);
+    const int64_t tiles_x = (jobs[i].cols + 63) / 64, tiles_y = (jobs[i].rows + 63) / 64;
+    if (tiles_x > INT32_MAX || tiles_y > INT32_MAX)
+      return fail(BSQ_ERR_UNSUPPORTED, "quant_mx: too many tiles");
+    const int64_t tiles = tiles_x * tiles_y;  // both factors below 2^31
     if (blocks + tiles > int64_t(INT32_MAX)) return fail(BSQ_ERR_UNSUPPORTED, "quant_mx: too many tiles");
+    j.tiles_x = int(tiles_x);
+    j.first = blocks;
     blocks += int(tiles);
   }
   if (J.n == 0) return ok();

@@ -20,6 +20,9 @@
  *     over them) at most 2^24, a batch of products at most 65535, and one
  *     product's output at most 2^31 - 1 tiles of 128 x 256 (far beyond any
  *     output that fits in memory); larger -> BSQ_ERR_UNSUPPORTED.
+ *   - No array a call reads or writes may hold more than 2^60 elements
+ *     (so that no size or offset overflows 64 bits); larger ->
+ *     BSQ_ERR_UNSUPPORTED.
  *   - A *_workspace_bytes query returns 0 for negative sizes and SIZE_MAX
  *     for sizes whose byte count would not fit (its call rejects them).
  *   - Non-finite inputs give unspecified results (the pages state all
@@ -135,7 +138,8 @@ bsq_status bsq_quant_mx(int64_t rows, int64_t cols, int axis, const void* src, i
  * int8 per-channel, scale and code formulas: s_b = max_i |x_bi| / 127
  * (float32), s_b = 1 when the row is all zero, q = clip(round(x / s),
  * -127, 127), round = nearest with ties to even.
- *   x [B, D] float32 -> x_q [B, D] int8, x_s [B] float32. */
+ *   x [B, D] float32 -> x_q [B, D] int8, x_s [B] float32.
+ * Rules: B <= 2^31 - 1 (one workgroup per row), else UNSUPPORTED. */
 bsq_status bsq_int8_quant_rows(int64_t B, int64_t D, const float* x, int8_t* x_q, float* x_s,
                                void* stream);
 

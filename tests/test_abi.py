@@ -230,6 +230,25 @@ def test_workspace_queries_never_wrap(L):
                                                   None), UNSUP, L)
 
 
+def test_element_count_limits(L):
+    """Extents whose element counts would overflow 64-bit sizes and offsets
+    (more than 2^60 elements in one array) are refused on the host, and
+    the int8 row quantizer's one-workgroup-per-row grid caps B at 2^31 - 1."""
+    big = 1 << 40
+    _expect(L.bsq_quant_fp8_rowblock(big, 1 << 30, 128, A16, A16, A16, None), UNSUP, L)
+    _expect(L.bsq_quant_fp8_tile(big, 1 << 30, 128, 128, A16, A16, A16, None), UNSUP, L)
+    _expect(L.bsq_quant_mx(big, 1 << 30, 0, A16, bsq.BSQ_F32, A16, bsq.BSQ_E4M3, A16, None), UNSUP, L)
+    _expect(L.bsq_quant_mx(big, 1 << 30, 1, A16, bsq.BSQ_F32, A16, bsq.BSQ_E4M3, A16, None), UNSUP, L)
+    _expect(L.bsq_int8_quant_cols(4, 1 << 62, A16, A16, A16, A16, None), UNSUP, L)
+    _expect(L.bsq_int8_quant_rows(1 << 31, 1, A16, A16, A16, None), UNSUP, L)
+    _expect(L.bsq_int8_quant_rows((1 << 31) - 1, 1, A16, A16, A16, None), DEVICE, L)
+    _expect(L.bsq_int8_quant_rows(4, 1 << 62, A16, A16, A16, None), UNSUP, L)
+    E4, E8, F32 = bsq.BSQ_E4M3, bsq.BSQ_E8M0, bsq.BSQ_F32
+    K = 1 << 24
+    _expect(L.bsq_scaled_matmul(65535, 1 << 30, 16, K, K // 32, K // 32, A16, E4, A16, E4, A16, A16, E8,
+                                A16, F32, None), UNSUP, L)
+
+
 def test_backward_split_validation(L):
     """The two-call backward: an operand is produced iff its codes pointer
     is given; a product is computed iff its output pointer is given."""
