@@ -141,9 +141,13 @@ __global__ void __launch_bounds__(256) k_fp8_rowblock(const float4* __restrict__
 }
 
 // ------------------------------------------------ fp8 128 x 128 tiles ----
-// One workgroup per tile, tiles numbered row-major along a one-dimensional
-// grid; each thread holds 64 values (16 float4) of the tile in registers
-// between the reduction and the encode.
+// One workgroup per tile along a one-dimensional grid; each thread holds 64
+// values (16 float4) of the tile in registers between the reduction and the
+// encode.  Workgroups are dealt to the 8 XCDs round-robin by linear id, and
+// linear id L takes tile (L % 8) * (T / 8) + L / 8 of the row-major order,
+// so each XCD works through a contiguous run of tiles (tiles past 8 (T / 8)
+// keep their own index).  Measured at 4096^2 with cold inputs: 15.5 us
+// against 15.6 us for the plain row-major order, same bytes.
 __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ src,
                                                      uint8_t* __restrict__ codes,
                                                      float* __restrict__ scales, int64_t cols) {
@@ -152,7 +156,8 @@ __global__ void __launch_bounds__(256) k_fp8_tile128(const float* __restrict__ s
   const int c4 = tx & 31;
   const int r0 = tx >> 5;
   const int64_t tiles_c = cols / 128;
-  const int64_t t = blockIdx.x;
+  const int64_t T = gridDim.x, per = T / 8, L = blockIdx.x;
+  const int64_t t = L < 8 * per ? (L % 8) * per + L / 8 : L;
   const int64_t row0 = (t / tiles_c) * 128;
   const int64_t col0 = (t % tiles_c) * 128 + 4 * c4;
   float4 v[16];
