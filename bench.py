@@ -417,7 +417,7 @@ def run_suite(args):
 
     last = {}
 
-    def time_launches(fn, n_iter, rotate=1, reps=5):
+    def time_launches(fn, n_iter, rotate=1, reps=20):
         """Median over `reps` batches of the per-launch time of a batch of
         n_iter back-to-back launches (the minimum is kept for the row)."""
         for i in range(3):
