@@ -248,6 +248,69 @@ def test_blockwise_is_deterministic():
     assert_bytes_equal(y1.view(np.uint32), y2.view(np.uint32), "two runs")
 
 
+def test_every_product_is_deterministic():
+    """Every product runs twice on the same inputs and gives the same bytes:
+    the few-tiles FP8 kernel, the MX batched product, the int8 composite
+    (whose column maxima are atomic maxima on float bits, an
+    order-independent operation), nvfp4 and the MXFP8 backward.  No kernel
+    sums in an order that depends on timing."""
+    torch = _torch()
+    say("determinism: few-tiles FP8")
+    a, b, sa, sb = _random_blockwise(237, 1024, 1024, 910)
+    y1, y2 = (host(_run_blockwise(a, b, sa, sb)) for _ in range(2))
+    assert_bytes_equal(y1.view(np.uint32), y2.view(np.uint32), "few-tiles FP8")
+
+    say("determinism: MX batched")
+    Bt, M, N, K = 2, 1000, 1024, 1024
+    a = to_dev(synth.random_fp8_codes((Bt, M, K), 911, "e4m3"))
+    b = to_dev(synth.random_fp8_codes((Bt, N, K), 912, "e4m3"))
+    sa = to_dev(synth.random_e8m0_codes((Bt, M, K // 32), 913))
+    sb = to_dev(synth.random_e8m0_codes((Bt, N, K // 32), 914))
+    ys = []
+    for _ in range(2):
+        y = filled((Bt, M, N), torch.float32, float("nan"))
+        bsq.bsq_scaled_matmul(a, b, sa, sb, y, lhs_dtype=bsq.BSQ_E4M3, rhs_dtype=bsq.BSQ_E4M3,
+                              scale_dtype=bsq.BSQ_E8M0)
+        ys.append(host(y))
+    assert_bytes_equal(ys[0].view(np.uint32), ys[1].view(np.uint32), "MX batched")
+
+    say("determinism: int8 composite")
+    B, Din, Dout = 512, 2048, 1024
+    x, w = synth.int8_workload(B, Din, Dout, 915, 916)
+    x, w = to_dev(x), to_dev(w)
+    outs = []
+    for _ in range(2):
+        wq = empty((Din, Dout), torch.int8)
+        ws = empty((Dout,), torch.float32)
+        xq = empty((B, Din), torch.int8)
+        xs = empty((B,), torch.float32)
+        y = filled((B, Dout), torch.float32, float("nan"))
+        work = empty((bsq.bsq_int8_workspace_bytes(Din, Dout),), torch.uint8)
+        bsq.bsq_int8_per_channel_matmul(x, w, wq, ws, xq, xs, y, work)
+        outs.append([host(t) for t in (wq, ws, xq, xs, y)])
+    for name, u, v in zip(("w_q", "w_s", "x_q", "x_s", "y"), outs[0], outs[1]):
+        assert_bytes_equal(u.view(np.uint8), v.view(np.uint8), "int8 " + name)
+
+    say("determinism: nvfp4")
+    Bt, M, N, K = 1, 500, 512, 1024
+    a = synth.random_e2m1_codes((Bt, M, K), 917)
+    b = synth.random_e2m1_codes((Bt, N, K), 918)
+    sa = synth.random_e4m3_scale_codes((Bt, M, K // 16), 919, 1, 14)
+    sb = synth.random_e4m3_scale_codes((Bt, N, K // 16), 920, 1, 14)
+    y1, y2 = (host(_run_nvfp4(a, b, sa, sb, torch.float32)[0]) for _ in range(2))
+    assert_bytes_equal(y1.view(np.uint32), y2.view(np.uint32), "nvfp4")
+
+    say("determinism: MXFP8 backward")
+    M, N, K = 512, 384, 640
+    dYb = synth.randn_bf16_bits((M, N), 921)
+    Wb = synth.randn_bf16_bits((N, K), 922)
+    Xb = synth.randn_bf16_bits((M, K), 923)
+    r1 = [host(t) for t in _run_backward(dYb, Wb, Xb, torch.bfloat16, bsq.BSQ_E5M2)]
+    r2 = [host(t) for t in _run_backward(dYb, Wb, Xb, torch.bfloat16, bsq.BSQ_E5M2)]
+    assert_bytes_equal(r1[0], r2[0], "backward dX")
+    assert_bytes_equal(r1[1], r2[1], "backward dW")
+
+
 def _hip():
     """The process's HIP runtime (the copy torch loaded), for raw events."""
     import ctypes
