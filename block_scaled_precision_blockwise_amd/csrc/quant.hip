@@ -282,22 +282,40 @@ struct MxJob {
 struct MxJobs {
   MxJob j[kMxJobs];
   int n;
+  // 1: a lone job that writes only the transposed output takes its tiles
+  // column by column, each XCD a contiguous run of them (workgroups are
+  // dealt to the 8 XCDs round-robin by linear id), so that the two tiles
+  // writing the halves of one output line run side by side on one XCD;
+  // 0: tiles row by row in launch order
+  int order;
 };
 
 template <int SRC_BF16, int CODE>
 __global__ void __launch_bounds__(256) k_mx_cols_t(MxJobs jobs) {
   constexpr int EMAX = CODE == 0 ? 8 : 15;
   __shared__ float tile[64][65];
+  int b = blockIdx.x;
+  if (jobs.order == 1) {
+    const int T = gridDim.x, per = T / 8;
+    b = b < 8 * per ? (b % 8) * per + b / 8 : b;
+  }
   int ji = 0;
 #pragma unroll
   for (int q = 1; q < kMxJobs; ++q)
-    if (q < jobs.n && int(blockIdx.x) >= jobs.j[q].first) ji = q;
+    if (q < jobs.n && b >= jobs.j[q].first) ji = q;
   const MxJob& J = jobs.j[ji];
-  const int t = int(blockIdx.x) - J.first;
+  const int t = b - J.first;
   const int64_t rows = J.rows, cols = J.cols;
   const int tx = threadIdx.x;
-  const int64_t r0 = int64_t(t / J.tiles_x) * 64;
-  const int64_t c0 = int64_t(t % J.tiles_x) * 64;
+  int64_t r0, c0;
+  if (jobs.order == 1) {
+    const int tiles_y = int((rows + 63) / 64);
+    r0 = int64_t(t % tiles_y) * 64;
+    c0 = int64_t(t / tiles_y) * 64;
+  } else {
+    r0 = int64_t(t / J.tiles_x) * 64;
+    c0 = int64_t(t % J.tiles_x) * 64;
+  }
   const bool both = J.row_codes != nullptr;
   // load: 64 rows x 64 cols, 8 values per thread-step, 2 steps
 #pragma unroll
@@ -826,6 +844,10 @@ bsq_status launch_mx_cols(const MxT* jobs, int n, bool src_bf16, bool e5m2, hipS
     blocks += int(tiles);
   }
   if (J.n == 0) return ok();
+  // measured at 8192x4096 bf16: 23.9 us against 24.8 row by row for a lone
+  // transposed job; the backward's three-job launch and a job that also
+  // writes rows were slower that way (79.7 against 64.8 us, 38.4 against 36.2)
+  J.order = (J.n == 1 && J.j[0].row_codes == nullptr) ? 1 : 0;
 #define BSQ_MXC(B, C) hipLaunchKernelGGL((k_mx_cols_t<B, C>), dim3(unsigned(blocks)), 256, 0, st, J)
   if (src_bf16) {
     if (e5m2) BSQ_MXC(1, 1); else BSQ_MXC(1, 0);
